@@ -1,0 +1,228 @@
+"""Benchmark of prompt-phase selection attention over INT8 paged K/V on one MI355X.
+
+A step is one pass of the whole path over one prompt chunk: the union kernel
+then the attention kernel, on inputs already resident in HBM. The default
+workload is the 32K-context chunk: 8,192 query positions (24,576..32,767),
+4 KV heads x 12 query heads, head_dim 128, INT8 K/V with per-cell scales behind
+a shuffled page table of 512 pages, selections of 3 sinks + own block + 31
+drifting blocks (drift 0.05), cap 2,051.
+
+Prints ONE JSON line: the metric (selected query-head-cells per second; prompt
+positions per second beside it), the roofline of the dominant kernel measured
+with HIP events on its own stream, and the CPU oracle timed on a bounded sample
+of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix
+# algorithmic bytes per union cell per (group, KV head) workgroup:
+#   K row 128 + V row 128 + k_scale 4 + v_scale 4 (the union K/V bytes: 264)
+#   + union cell index 4 + chooser byte 1 + page-table entry 4
+UNION_KV_BYTES = 264
+UNION_CELL_BYTES = UNION_KV_BYTES + 4 + 1 + 4
+ROW_BYTES = 128 * 4 * 2        # q in + out, per (query position, query head)
+FLOP_PER_CELL_ROW = 4 * 128    # QK^T and PV, per (union cell, row)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ctx32k_drift005")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="query positions of the oracle's timed sample (0 = skip)")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for rocprofv3: no CPU leg, plus a 512 MiB copy for counter calibration")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_top_selection_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload_name: str):
+    """HBM bytes per prefill launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "prefill_%s_counters.json" % workload_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this path is measured on a single MI355X "
+              "(the work units are independent; see the sharding notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import sparse_top_selection_amd as sa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    inp = synth.as_problem(synth.generate(w))
+
+    # work counts of this input
+    sel, sel_len, pt = inp["sel"], inp["sel_len"], inp["page_table"]
+    resident_cells = 0
+    for j in range(w.n_q):
+        row = np.unique(sel[j, :sel_len[j]])
+        resident_cells += int(np.count_nonzero(pt[row // 64] >= 0))
+    q_head_cells = resident_cells * w.n_qh
+
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+         for k in ("q", "k_pool", "v_pool", "k_scale", "v_scale", "page_table", "sel", "sel_len")}
+    g = w.n_groups
+    cap = w.sel_cap
+    cells = torch.empty((g, 8 * cap), dtype=torch.int32, device=dev)
+    mask = torch.empty((g, 8 * cap), dtype=torch.uint8, device=dev)
+    length = torch.empty(g, dtype=torch.int32, device=dev)
+    out = torch.empty_like(t["q"])
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dims = sa.make_dims(w.n_ctx, w.n_q, w.n_kv, w.pool_pages, sel_cap=cap)
+    scale = float(inp["softmax_scale"])
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sa.sel_attn_build_union(dims, t["sel"], t["sel_len"], cells, mask, length, status, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        sa.sel_attn_prefill(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"],
+                            t["page_table"], cells, mask, length, scale, out, status, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sa.check_status(status)
+
+    steps = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sa.check_status(status)
+    union_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = wall / steps * 1e3
+
+    lens = length.cpu().numpy().astype(np.int64)
+    union_cells = int(lens.sum())
+    alg_bytes = union_cells * w.n_kv * UNION_CELL_BYTES + w.n_q * w.n_qh * ROW_BYTES
+    union_kv_bytes = union_cells * w.n_kv * UNION_KV_BYTES
+    flops = union_cells * w.n_kv * 96 * FLOP_PER_CELL_ROW
+    achieved = alg_bytes / (prefill_ms * 1e-3) / 1e9
+    traffic = counter_traffic(w.name)
+
+    if args.profile:
+        # plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": "selected query-head-cells/s (32K-context prompt chunk)",
+        "value": q_head_cells / (ms_per_step * 1e-3),
+        "unit": "query-head-cells/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 K/V, fp16 products, fp32 softmax and sums",
+        "data": "synthetic (seeded; shapes of the pages' parity self-test)",
+        "config": {
+            "workload": w.name,
+            "n_ctx": w.n_ctx, "query_positions": w.n_q, "first_position": w.first_pos,
+            "kv_heads": w.n_kv, "q_heads_per_kv": w.q_per_kv, "head_dim": w.head_dim,
+            "page_size": w.page_size, "pool_pages": w.pool_pages, "sel_cap": w.sel_cap,
+            "drift": w.drift, "parallelism": "single GPU",
+        },
+        "prompt_positions_per_s": w.n_q / (ms_per_step * 1e-3),
+        "kernels_ms": {"union_build": union_ms, "prefill": prefill_ms},
+        "union": {"cells": union_cells, "mean_per_group": union_cells / g,
+                  "ratio_to_mean_selection": (union_cells / g) / float(sel_len.mean())},
+        "union_kv_GBps": union_kv_bytes / (prefill_ms * 1e-3) / 1e9,
+        "union_kv_frac_of_hbm_peak": union_kv_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "mfma_frac_of_f16_peak": flops / (prefill_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS,
+        "roofline": {
+            "kernel": "sel_attn_prefill_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+        "source_hash": source_hash(),
+    }
+
+    if args.cpu_rows > 0 and not args.profile:
+        import oracle
+        n_rows = min(args.cpu_rows, w.n_q)
+        rows = np.arange(n_rows, dtype=np.int32)
+        cores = oracle.max_threads()
+        c0 = time.perf_counter()
+        ref = oracle.attention_of(inp, rows=rows, n_threads=cores)
+        cpu_s = time.perf_counter() - c0
+        sample_cells = 0
+        for j in rows:
+            row = np.unique(sel[j, :sel_len[j]])
+            sample_cells += int(np.count_nonzero(pt[row // 64] >= 0))
+        got = out[:n_rows].cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        result["cpu_baseline"] = {
+            "value": sample_cells * w.n_qh / cpu_s,
+            "unit": "query-head-cells/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": "query positions 0..%d of the same chunk (%d of %d), FP64 per-position "
+                      "gather, %.1f s" % (n_rows - 1, n_rows, w.n_q, cpu_s),
+            "positions_per_s": n_rows / cpu_s,
+        }
+        result["parity_on_cpu_sample"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                                          "out_rms": float(np.sqrt(np.mean(ref ** 2)))}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * sel_attn.h - C ABI of libselattn.so: prompt-phase selection attention over
+ * INT8 paged K/V, hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * Page cited: #2808 "sycl: prompt attention over 8-query selection unions on
+ * XMX (opt-in STRATA_PROMPT_ATTN_UNION=1)".
+ *
+ * The method (section Summary): each query position attends only to the cells
+ * it selected. Groups of 8 neighbouring positions share one sorted union of
+ * their selections; every union cell carries a byte whose bit i says whether
+ * position i of the group chose it (section Extra Notes: an int32 cell plus a
+ * separate mask byte). K and V are INT8 behind a page table; 64-cell chunks of
+ * the union are dequantised once and multiplied on matrix cores with FP32 sums
+ * for all 96 rows of a group (8 positions x 12 query heads of one KV head); in
+ * the online softmax a cell counts as -inf for the positions that did not
+ * choose it, so every position attends to exactly its own cells.
+ *
+ * One pass of the path is two calls on one stream:
+ *   sel_attn_build_union  selections -> per-group union, masks, lengths
+ *   sel_attn_prefill      union + q + paged INT8 K/V -> attention output
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array pointers are DEVICE pointers owned by the caller. The library
+ *   allocates no device memory, keeps no state between calls except a cached
+ *   per-device architecture check, and enqueues its kernels asynchronously on
+ *   `stream` (NULL = the null stream). Inputs are only read.
+ * - Return value: SEL_ATTN_OK when the kernels were enqueued; a negative code
+ *   when nothing was enqueued. sel_attn_last_error() then describes why.
+ * - Errors that need the data to detect (a cell out of range, a bad length, a
+ *   page-table entry past the pool) cannot be returned synchronously. The
+ *   kernels OR SEL_ATTN_STATUS_* bits into *status (a device uint32 that the
+ *   caller zeroes beforehand and reads after synchronising the stream). Outputs
+ *   of the groups concerned are then unspecified, but every access stays in
+ *   bounds.
+ * - Calls are deterministic: identical inputs give bitwise-identical outputs.
+ *   Calls on different streams that write different outputs may overlap.
+ */
+#ifndef SEL_ATTN_H_
+#define SEL_ATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define SEL_ATTN_OK 0
+#define SEL_ATTN_EINVAL (-1)       /* null or misaligned pointer, or a size out of range */
+#define SEL_ATTN_EUNSUPPORTED (-2) /* a shape this build does not implement, or a device that is not gfx950 */
+#define SEL_ATTN_ELAUNCH (-3)      /* a HIP call failed (device query or kernel launch) */
+
+/* Bits the kernels OR into *status. */
+#define SEL_ATTN_STATUS_CELL_RANGE 1u  /* a selected or union cell outside [0, n_ctx) */
+#define SEL_ATTN_STATUS_SEL_LEN 2u     /* sel_len[j] outside [0, sel_cap] */
+#define SEL_ATTN_STATUS_PAGE_RANGE 4u  /* page_table entry >= n_pages (or < -1) */
+#define SEL_ATTN_STATUS_UNION_LEN 8u   /* union_len[g] outside [0, 8*sel_cap] */
+#define SEL_ATTN_STATUS_V_SCALE 16u    /* a v_scale of a used cell with |v_scale| >= 4 or not finite */
+
+/* Shapes this build implements. */
+#define SEL_ATTN_HEAD_DIM 128
+#define SEL_ATTN_PAGE_SIZE 64
+#define SEL_ATTN_Q_PER_KV 12
+#define SEL_ATTN_GROUP 8           /* positions per union group */
+
+typedef struct sel_attn_dims {
+  int32_t n_ctx;     /* logical context length in cells, >= 1; page_table has
+                        ceil(n_ctx / page_size) entries */
+  int32_t n_q;       /* query positions in this call, >= 0 (0 = nothing to do).
+                        Group g holds query indices [8g, 8g+8) clipped to n_q; the
+                        last group may be ragged. Groups start at query index 0. */
+  int32_t n_kv;      /* KV heads, >= 1 */
+  int32_t q_per_kv;  /* query heads per KV head; must be 12. Query head h reads
+                        KV head h / 12 */
+  int32_t head_dim;  /* must be 128 */
+  int32_t page_size; /* cells per page; must be 64 */
+  int32_t sel_cap;   /* row stride of sel, >= 1 (2051 in the headline workloads);
+                        each group's union rows have stride 8 * sel_cap */
+  int32_t n_pages;   /* physical pages in each pool, >= 1 */
+} sel_attn_dims;
+
+/*
+ * sel_attn_build_union - the union step (section Summary: a first kernel builds,
+ * for every 8 neighbouring positions, the sorted union of their selected cells,
+ * marking each cell with the positions that chose it; section What changed:
+ * one work-group per 8 positions with local bitmaps).
+ *
+ *   sel          const int32 [n_q][sel_cap]   selected logical cells of each
+ *                                             query index; any order, repeats
+ *                                             allowed (a cell counts once)
+ *   sel_len      const int32 [n_q]            valid entries of each row
+ *   union_cells  int32 [G][8*sel_cap]         out: ascending distinct cells of
+ *                                             group g in [0, union_len[g])
+ *   union_mask   uint8 [G][8*sel_cap]         out: bit i set iff query index
+ *                                             8g+i chose the cell
+ *   union_len    int32 [G]                    out: size of group g's union
+ *   status       uint32 [1]                   in/out: OR of SEL_ATTN_STATUS_*
+ *   G = ceil(n_q / 8). Entries past union_len[g] are left untouched.
+ *   Residency is not consulted: the union depends on the selections alone.
+ *   Errors: a cell outside [0, n_ctx) is dropped and sets CELL_RANGE; a length
+ *   outside [0, sel_cap] is clamped and sets SEL_LEN.
+ *   Alignment: 4 bytes for the int32 arrays.
+ */
+int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32_t* sel_len,
+                         int32_t* union_cells, uint8_t* union_mask, int32_t* union_len,
+                         uint32_t* status, hipStream_t stream);
+
+/*
+ * sel_attn_prefill - the attention step over each group's union (section
+ * Summary: INT8 K/V of 64-cell chunks of the union dequantised once, S^T = K Q^T
+ * and O += P V on matrix cores with FP32 sums for the group's 96 rows, cells the
+ * row's position did not choose set to -inf in the online softmax; section
+ * What changed: one work-group per group of 8 positions and KV head).
+ *
+ *   q            const float [n_q][n_kv*12][128]        queries (rounded to
+ *                                                       FP16 for the products)
+ *   k_pool       const int8  [n_pages][n_kv][64][128]   keys, page-major, then
+ *   v_pool       const int8  [n_pages][n_kv][64][128]   KV head, cell, dim
+ *   k_scale      const float [n_pages][n_kv][64]        per cell and KV head:
+ *   v_scale      const float [n_pages][n_kv][64]        k = k_int8 * k_scale
+ *   page_table   const int32 [ceil(n_ctx/64)]           physical page of each
+ *                                                       logical page; -1 = not
+ *                                                       resident (its cells are
+ *                                                       masked for everyone)
+ *   union_cells, union_mask, union_len                  as written by
+ *                                                       sel_attn_build_union
+ *                                                       with the same dims
+ *   softmax_scale                                       multiplies q.k (e.g.
+ *                                                       1/sqrt(128))
+ *   out          float [n_q][n_kv*12][128]              out: softmax-weighted
+ *                                                       sum of dequantised V
+ *                                                       over the position's own
+ *                                                       resident cells; 0 when
+ *                                                       it has none
+ *   status       uint32 [1]                             in/out, as above
+ *   Precision: Q, dequantised K, V and the probabilities enter the products as
+ *   FP16 (round to nearest even); scores, softmax and sums are FP32. K and V
+ *   integers are exact in FP16; their scales are applied in FP32.
+ *   Supported scales: |v_scale| < 4 (other values set V_SCALE); k_scale any
+ *   finite value.
+ *   Errors: CELL_RANGE, PAGE_RANGE, UNION_LEN, V_SCALE as listed above; a bad
+ *   cell or page is treated as not resident.
+ *   Alignment: q, out, k_pool, v_pool 16 bytes; the rest 4 bytes (mask 1).
+ */
+int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                     const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                     const int32_t* page_table, const int32_t* union_cells,
+                     const uint8_t* union_mask, const int32_t* union_len,
+                     float softmax_scale, float* out, uint32_t* status, hipStream_t stream);
+
+/*
+ * sel_attn_last_error - text describing the last nonzero return of an entry
+ * point on the calling thread ("" if none). The pointer stays valid until the
+ * thread's next call into the library.
+ */
+const char* sel_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEL_ATTN_H_ */

@@ -1,0 +1,222 @@
+"""Python binding of libselattn.so: prompt-phase selection attention over INT8
+paged K/V on gfx950.
+
+Argument marshalling only. Every step of the path runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream. There is no
+fallback: importing this package fails loudly when libselattn.so is missing,
+and every call raises when the library returns an error code.
+
+The functions named like the C entry points (sel_attn_build_union,
+sel_attn_prefill, sel_attn_last_error) take preallocated device tensors and
+mirror include/sel_attn.h one to one. build_union(), prefill() and
+check_status() are conveniences that allocate outputs and read the status word.
+
+Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
+(opt-in STRATA_PROMPT_ATTN_UNION=1)", section Summary.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libselattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libselattn.so is not built (%s); run `python -m sparse_top_selection_amd.build`" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK = 0
+EINVAL = -1
+EUNSUPPORTED = -2
+ELAUNCH = -3
+
+STATUS_CELL_RANGE = 1
+STATUS_SEL_LEN = 2
+STATUS_PAGE_RANGE = 4
+STATUS_UNION_LEN = 8
+STATUS_V_SCALE = 16
+
+HEAD_DIM = 128
+PAGE_SIZE = 64
+Q_PER_KV = 12
+GROUP = 8
+
+EXPORTED = ("sel_attn_build_union", "sel_attn_prefill", "sel_attn_last_error")
+
+
+class Dims(ctypes.Structure):
+    """sel_attn_dims of include/sel_attn.h."""
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_ctx", "n_q", "n_kv", "q_per_kv", "head_dim", "page_size", "sel_cap",
+                 "n_pages")]
+
+
+def make_dims(n_ctx: int, n_q: int, n_kv: int, n_pages: int, sel_cap: int = 2051,
+              q_per_kv: int = Q_PER_KV, head_dim: int = HEAD_DIM,
+              page_size: int = PAGE_SIZE) -> Dims:
+    return Dims(n_ctx, n_q, n_kv, q_per_kv, head_dim, page_size, sel_cap, n_pages)
+
+
+_p = ctypes.c_void_p
+_lib.sel_attn_build_union.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p]
+_lib.sel_attn_build_union.restype = ctypes.c_int
+_lib.sel_attn_prefill.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                  ctypes.c_float, _p, _p, _p]
+_lib.sel_attn_prefill.restype = ctypes.c_int
+_lib.sel_attn_last_error.argtypes = []
+_lib.sel_attn_last_error.restype = ctypes.c_char_p
+
+
+class SelAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+def sel_attn_last_error() -> str:
+    return _lib.sel_attn_last_error().decode()
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise SelAttnError(rc, sel_attn_last_error())
+
+
+def sel_attn_build_union(dims: Dims, sel, sel_len, union_cells, union_mask, union_len, status,
+                         stream=None) -> None:
+    """Enqueue the union step (see include/sel_attn.h). Tensors or raw device pointers."""
+    _check(_lib.sel_attn_build_union(ctypes.byref(dims), _ptr(sel), _ptr(sel_len),
+                                     _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
+                                     _ptr(status), _stream(stream)))
+
+
+def sel_attn_prefill(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
+                     union_mask, union_len, softmax_scale: float, out, status,
+                     stream=None) -> None:
+    """Enqueue the attention step (see include/sel_attn.h). Tensors or raw device pointers."""
+    _check(_lib.sel_attn_prefill(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(page_table),
+                                 _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
+                                 ctypes.c_float(float(softmax_scale)), _ptr(out), _ptr(status),
+                                 _stream(stream)))
+
+
+# --------------------------------------------------------------------------
+# conveniences over torch tensors
+# --------------------------------------------------------------------------
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims (got %s)" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+
+
+def new_status(device) -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def check_status(status: torch.Tensor) -> int:
+    """Synchronise on the status word and raise on any set bit."""
+    v = int(status.item()) & 0xFFFFFFFF
+    if v:
+        names = [n for n, b in (("CELL_RANGE", 1), ("SEL_LEN", 2), ("PAGE_RANGE", 4),
+                                ("UNION_LEN", 8), ("V_SCALE", 16)) if v & b]
+        raise SelAttnError(v, "device status: " + "|".join(names))
+    return v
+
+
+def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, status=None, stream=None,
+                out=None):
+    """Union of every group of 8 query indices. Returns (cells, mask, length, status)."""
+    dev = sel.device
+    _need(sel, "sel", torch.int32, 2, None)
+    _need(sel_len, "sel_len", torch.int32, 1, dev)
+    n_q, cap = sel.shape
+    if sel_len.shape[0] != n_q:
+        raise ValueError("sel_len must have n_q entries")
+    g = (n_q + 7) // 8
+    if out is None:
+        cells = torch.empty((g, 8 * cap), dtype=torch.int32, device=dev)
+        mask = torch.empty((g, 8 * cap), dtype=torch.uint8, device=dev)
+        length = torch.empty(g, dtype=torch.int32, device=dev)
+    else:
+        cells, mask, length = out
+    if status is None:
+        status = new_status(dev)
+    dims = make_dims(n_ctx, n_q, 1, 1, sel_cap=cap)
+    sel_attn_build_union(dims, sel, sel_len, cells, mask, length, status, stream)
+    return cells, mask, length, status
+
+
+def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_mask, union_len,
+            softmax_scale: float, n_ctx: int, status=None, stream=None, out=None):
+    """Attention over each group's union. Returns (out, status)."""
+    dev = q.device
+    _need(q, "q", torch.float32, 3, None)
+    for name, t, dt, nd in (("k_pool", k_pool, torch.int8, 4), ("v_pool", v_pool, torch.int8, 4),
+                            ("k_scale", k_scale, torch.float32, 3),
+                            ("v_scale", v_scale, torch.float32, 3),
+                            ("page_table", page_table, torch.int32, 1),
+                            ("union_cells", union_cells, torch.int32, 2),
+                            ("union_mask", union_mask, torch.uint8, 2),
+                            ("union_len", union_len, torch.int32, 1)):
+        _need(t, name, dt, nd, dev)
+    n_q, n_qh, hd = q.shape
+    n_pages, n_kv, ps, hd2 = k_pool.shape
+    if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != (n_pages, n_kv, ps) or \
+            tuple(v_scale.shape) != (n_pages, n_kv, ps):
+        raise ValueError("pool / scale shapes disagree")
+    if hd2 != hd or n_qh != n_kv * Q_PER_KV:
+        raise ValueError("q is [n_q][n_kv*12][head_dim] with the pools' n_kv and head_dim")
+    if page_table.shape[0] < -(-n_ctx // ps):
+        raise ValueError("page_table needs ceil(n_ctx / page_size) entries")
+    g = (n_q + 7) // 8
+    if union_len.shape[0] != g or union_cells.shape[0] != g or union_cells.shape[1] % 8 != 0 \
+            or union_mask.shape != union_cells.shape:
+        raise ValueError("union arrays must be [ceil(n_q/8)][8*sel_cap]")
+    cap = union_cells.shape[1] // 8
+    if out is None:
+        out = torch.empty_like(q)
+    if status is None:
+        status = new_status(dev)
+    dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=cap, head_dim=hd, page_size=ps)
+    sel_attn_prefill(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
+                     union_mask, union_len, softmax_scale, out, status, stream)
+    return out, status
+
+
+def attention(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+              softmax_scale: float, n_ctx: int, stream=None):
+    """One pass of the whole path (union, then attention). Returns (out, union, status)."""
+    cells, mask, length, status = build_union(sel, sel_len, n_ctx, stream=stream)
+    out, status = prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, cells, mask, length,
+                          softmax_scale, n_ctx, status=status, stream=stream)
+    return out, (cells, mask, length), status

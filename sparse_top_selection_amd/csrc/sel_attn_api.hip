@@ -1,0 +1,179 @@
+// Host side of libselattn.so: argument checks, the gfx950 device check, kernel
+// launches and per-thread error text. Every check that needs no data runs here,
+// before anything is enqueued; checks that need the data run in the kernels and
+// report through the caller's status word.
+//
+// Page: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
+// section Summary (the union path runs for INT8 KV on one card family and any
+// other case takes another path with a one-line reason) and section Extra Notes
+// (other parts are refused by a device check). Here there is a single path: an
+// unsupported case returns an error code and a reason instead.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "sel_attn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Shapes the kernels implement, and sizes whose offsets fit the kernels' index math.
+int check_dims(const sel_attn_dims* d, const char* who) {
+  if (!d) return fail(SEL_ATTN_EINVAL, "%s: dims is NULL", who);
+  if (d->n_ctx < 1) return fail(SEL_ATTN_EINVAL, "%s: n_ctx must be >= 1 (got %d)", who, d->n_ctx);
+  if (d->n_q < 0) return fail(SEL_ATTN_EINVAL, "%s: n_q must be >= 0 (got %d)", who, d->n_q);
+  if (d->n_kv < 1) return fail(SEL_ATTN_EINVAL, "%s: n_kv must be >= 1 (got %d)", who, d->n_kv);
+  if (d->sel_cap < 1) return fail(SEL_ATTN_EINVAL, "%s: sel_cap must be >= 1 (got %d)", who, d->sel_cap);
+  if (d->n_pages < 1) return fail(SEL_ATTN_EINVAL, "%s: n_pages must be >= 1 (got %d)", who, d->n_pages);
+  if (d->head_dim != SEL_ATTN_HEAD_DIM)
+    return fail(SEL_ATTN_EUNSUPPORTED, "%s: head_dim %d not supported (only %d)", who, d->head_dim,
+                SEL_ATTN_HEAD_DIM);
+  if (d->page_size != SEL_ATTN_PAGE_SIZE)
+    return fail(SEL_ATTN_EUNSUPPORTED, "%s: page_size %d not supported (only %d)", who, d->page_size,
+                SEL_ATTN_PAGE_SIZE);
+  if (d->q_per_kv != SEL_ATTN_Q_PER_KV)
+    return fail(SEL_ATTN_EUNSUPPORTED, "%s: q_per_kv %d not supported (only %d)", who, d->q_per_kv,
+                SEL_ATTN_Q_PER_KV);
+  // union rows of 8*sel_cap int32 cells: the per-group length must fit an int32
+  if ((int64_t)d->sel_cap * 8 > INT32_MAX)
+    return fail(SEL_ATTN_EINVAL, "%s: sel_cap %d too large", who, d->sel_cap);
+  // pool rows are indexed as int32 (phys * n_kv + h) * 64 + slot
+  if ((int64_t)d->n_pages * d->n_kv * SEL_ATTN_PAGE_SIZE > INT32_MAX)
+    return fail(SEL_ATTN_EINVAL, "%s: pool of %d pages x %d KV heads too large", who, d->n_pages,
+                d->n_kv);
+  if ((int64_t)d->n_kv * SEL_ATTN_Q_PER_KV * ((int64_t)(d->n_q + 7) / 8) > INT32_MAX)
+    return fail(SEL_ATTN_EINVAL, "%s: n_q x n_kv too large", who);
+  return SEL_ATTN_OK;
+}
+
+// gfx950 only; the answer is cached per device ordinal.
+int check_device(const char* who) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  static std::mutex mu;
+  static int known[64];  // 0 = unknown, 1 = gfx950, 2 = other
+  if (dev < 0 || dev >= 64) return fail(SEL_ATTN_EUNSUPPORTED, "%s: device ordinal %d", who, dev);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess)
+        return fail(SEL_ATTN_ELAUNCH, "%s: hipGetDeviceProperties: %s", who, hipGetErrorString(e));
+      known[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    if (known[dev] != 1)
+      return fail(SEL_ATTN_EUNSUPPORTED, "%s: device %d is not gfx950", who, dev);
+  }
+  return SEL_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sel_attn_last_error(void) { return g_err; }
+
+int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32_t* sel_len,
+                         int32_t* union_cells, uint8_t* union_mask, int32_t* union_len,
+                         uint32_t* status, hipStream_t stream) {
+  static const char* who = "sel_attn_build_union";
+  int rc = check_dims(d, who);
+  if (rc) return rc;
+  if (!status) return fail(SEL_ATTN_EINVAL, "%s: status is NULL", who);
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
+  if (!sel || !sel_len || !union_cells || !union_mask || !union_len)
+    return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
+  if (!aligned(sel, 4) || !aligned(sel_len, 4) || !aligned(union_cells, 4) ||
+      !aligned(union_len, 4) || !aligned(status, 4))
+    return fail(SEL_ATTN_EINVAL, "%s: int32 arrays must be 4-byte aligned", who);
+  rc = check_device(who);
+  if (rc) return rc;
+  selattn::UnionArgs a;
+  a.sel = sel;
+  a.sel_len = sel_len;
+  a.union_cells = union_cells;
+  a.union_mask = union_mask;
+  a.union_len = union_len;
+  a.status = status;
+  a.n_ctx = d->n_ctx;
+  a.n_q = d->n_q;
+  a.sel_cap = d->sel_cap;
+  hipError_t e = selattn::launch_union_build(a, stream);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SEL_ATTN_OK;
+}
+
+int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                     const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                     const int32_t* page_table, const int32_t* union_cells,
+                     const uint8_t* union_mask, const int32_t* union_len, float softmax_scale,
+                     float* out, uint32_t* status, hipStream_t stream) {
+  static const char* who = "sel_attn_prefill";
+  int rc = check_dims(d, who);
+  if (rc) return rc;
+  if (!status) return fail(SEL_ATTN_EINVAL, "%s: status is NULL", who);
+  if (!isfinite(softmax_scale))
+    return fail(SEL_ATTN_EINVAL, "%s: softmax_scale must be finite", who);
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
+  if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !union_cells ||
+      !union_mask || !union_len || !out)
+    return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(SEL_ATTN_EINVAL, "%s: q, out, k_pool and v_pool must be 16-byte aligned", who);
+  if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(page_table, 4) ||
+      !aligned(union_cells, 4) || !aligned(union_len, 4) || !aligned(status, 4))
+    return fail(SEL_ATTN_EINVAL, "%s: scale and int32 arrays must be 4-byte aligned", who);
+  rc = check_device(who);
+  if (rc) return rc;
+  selattn::PrefillArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.page_table = page_table;
+  a.union_cells = union_cells;
+  a.union_mask = union_mask;
+  a.union_len = union_len;
+  a.out = out;
+  a.status = status;
+  a.score_scale = softmax_scale * 1.4426950408889634f;
+  a.n_ctx = d->n_ctx;
+  a.n_q = d->n_q;
+  a.n_kv = d->n_kv;
+  a.n_pages = d->n_pages;
+  a.sel_cap = d->sel_cap;
+  a.n_groups = (d->n_q + 7) / 8;
+  const int64_t n_wg = (int64_t)a.n_groups * d->n_kv;
+  a.per_xcd = (int32_t)((n_wg + 7) / 8);
+  hipError_t e = selattn::launch_prefill(a, stream);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SEL_ATTN_OK;
+}
+
+}  // extern "C"

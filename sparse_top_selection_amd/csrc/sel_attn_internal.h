@@ -1,0 +1,48 @@
+// Internal declarations shared by the HIP sources of libselattn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sel_attn.h"
+
+namespace selattn {
+
+struct UnionArgs {
+  const int32_t* sel;
+  const int32_t* sel_len;
+  int32_t* union_cells;
+  uint8_t* union_mask;
+  int32_t* union_len;
+  uint32_t* status;
+  int32_t n_ctx;
+  int32_t n_q;
+  int32_t sel_cap;
+};
+
+struct PrefillArgs {
+  const float* q;
+  const int8_t* k_pool;
+  const int8_t* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* page_table;
+  const int32_t* union_cells;
+  const uint8_t* union_mask;
+  const int32_t* union_len;
+  float* out;
+  uint32_t* status;
+  float score_scale;   // softmax_scale * log2(e): scores go straight into exp2
+  int32_t n_ctx;
+  int32_t n_q;
+  int32_t n_kv;
+  int32_t n_pages;
+  int32_t sel_cap;
+  int32_t n_groups;
+  int32_t per_xcd;     // workgroups each XCD walks through (grid = 8 * per_xcd)
+};
+
+hipError_t launch_union_build(const UnionArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace selattn

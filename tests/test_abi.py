@@ -1,0 +1,94 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sel_attn.h")
+LIB = os.path.join(ROOT, "sparse_top_selection_amd", "libselattn.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sel_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["sel_attn_build_union", "sel_attn_last_error",
+                                    "sel_attn_prefill"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_names_match_header():
+    import sparse_top_selection_amd as sa
+    assert sorted(sa.EXPORTED) == declared_functions()
+    for name in declared_functions():
+        assert callable(getattr(sa, name))
+
+
+def _dims(**kw):
+    import sparse_top_selection_amd as sa
+    base = dict(n_ctx=1024, n_q=16, n_kv=2, n_pages=16)
+    base.update(kw)
+    d = sa.make_dims(base.pop("n_ctx"), base.pop("n_q"), base.pop("n_kv"), base.pop("n_pages"),
+                     **base)
+    return d
+
+
+FAKE = 1 << 20   # never dereferenced: every case below fails on the host first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(q_per_kv=8), -2),
+    (dict(n_ctx=0), -1), (dict(n_q=-1), -1), (dict(n_kv=0), -1), (dict(sel_cap=0), -1),
+    (dict(n_pages=0), -1), (dict(n_pages=1 << 25, n_kv=4), -1),
+])
+def test_bad_dims_rejected_on_host(kw, code):
+    import sparse_top_selection_amd as sa
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_build_union(_dims(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == code
+    assert "sel_attn_build_union" in sa.sel_attn_last_error()
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_prefill(_dims(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == code
+
+
+def test_null_and_misaligned_pointers_rejected_on_host():
+    import sparse_top_selection_amd as sa
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_build_union(_dims(), FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_build_union(_dims(), FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:   # q must be 16-byte aligned
+        sa.sel_attn_prefill(_dims(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:   # status is required
+        sa.sel_attn_prefill(_dims(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            0.1, FAKE, None, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:   # non-finite softmax scale
+        sa.sel_attn_prefill(_dims(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            float("inf"), FAKE, FAKE, stream=0)
+    assert e.value.code == -1
+
+
+def test_empty_query_batch_is_a_no_op():
+    import sparse_top_selection_amd as sa
+    sa.sel_attn_build_union(_dims(n_q=0), None, None, None, None, None, FAKE, stream=0)
+    sa.sel_attn_prefill(_dims(n_q=0), None, None, None, None, None, None, None, None, None, 0.1,
+                        None, FAKE, stream=0)
+    assert sa.sel_attn_last_error() == ""

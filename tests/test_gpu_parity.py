@@ -1,0 +1,212 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Union: bit-exact (cells, masks, lengths). Attention: max abs <= 8e-3 and mean
+abs <= 1e-3 against FP64 on every workload, plus an exact-arithmetic case that
+catches a single wrong cell or mask bit, non-resident pages, empty rows, ragged
+groups, long contexts (several union windows) and a bitwise rerun.
+Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
+section Accuracy (the parity self-test's cases).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    if not name.startswith("gfx950"):
+        pytest.skip("not gfx950: %s" % name)
+
+
+import gpu_helpers as H  # noqa: E402  (imports the binding; only after the skip check)
+import sparse_top_selection_amd as sa  # noqa: E402
+
+
+# ----------------------------------------------------------------------------- union
+@pytest.mark.parametrize("idx", range(5))
+def test_union_bit_exact_on_workloads(idx):
+    w = synth.workload(idx)
+    d = synth.as_problem(synth.generate(w, with_q=False, with_pools=False))
+    print("case", w.name, flush=True)
+    sel = torch.from_numpy(d["sel"]).cuda()
+    sel_len = torch.from_numpy(d["sel_len"]).cuda()
+    cells, mask, length, status = sa.build_union(sel, sel_len, w.n_ctx)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
+                         oracle.union(d["sel"], d["sel_len"], w.n_ctx))
+
+
+@pytest.mark.parametrize("n_ctx,n_q,seed", [(300, 45, 1), (5000, 33, 2), (70000, 17, 3),
+                                            (200001, 9, 4), (64, 8, 5), (1, 3, 6)])
+def test_union_bit_exact_edge_cases(n_ctx, n_q, seed):
+    """Ragged groups, repeats, unsorted rows, empty rows, contexts over one window."""
+    print("case", n_ctx, n_q, seed, flush=True)
+    rng = np.random.default_rng(seed)
+    cap = 2051
+    sel = np.full((n_q, cap), -1, np.int32)
+    sel_len = np.zeros(n_q, np.int32)
+    for j in range(n_q):
+        kind = j % 4
+        if kind == 0:
+            row = np.zeros(0, np.int32)
+        elif kind == 1:
+            row = np.array([n_ctx - 1], np.int32)          # a cell on the last page
+        else:
+            n = int(rng.integers(1, cap + 1))
+            row = rng.integers(0, n_ctx, size=n).astype(np.int32)   # with repeats
+        sel[j, :row.size] = row
+        sel_len[j] = row.size
+    cells, mask, length, status = sa.build_union(torch.from_numpy(sel).cuda(),
+                                                 torch.from_numpy(sel_len).cuda(), n_ctx)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
+                         oracle.union(sel, sel_len, n_ctx))
+
+
+def test_union_flags_bad_cells_and_lengths():
+    sel = np.full((10, 16), -1, np.int32)
+    sel_len = np.full(10, 3, np.int32)
+    sel[:, :3] = [1, 2, 3]
+    sel[4, 1] = 100           # outside [0, n_ctx)
+    sel[6, 0] = -5
+    sel_len[8] = 17           # over the cap: clamped
+    cells, mask, length, status = sa.build_union(torch.from_numpy(sel).cuda(),
+                                                 torch.from_numpy(sel_len).cuda(), 100)
+    torch.cuda.synchronize()
+    st = int(status.item())
+    assert st & sa.STATUS_CELL_RANGE and st & sa.STATUS_SEL_LEN
+    # the bad cells are dropped, the rest of the group is intact
+    assert length.cpu().tolist()[0] == 3
+    assert cells.cpu().numpy()[0, :3].tolist() == [1, 2, 3]
+    assert mask.cpu().numpy()[0, :3].tolist() == [0xFF ^ 0x40, 0xFF ^ 0x10, 0xFF]
+
+
+# ------------------------------------------------------------------------- attention
+def _check_problem(d, rows=None, what=""):
+    dev = H.to_device(d)
+    out, cells, mask, length, status = H.run_path(d, dev)
+    assert status == 0, status
+    H.assert_union_equal(cells, mask, length, oracle.union(d["sel"], d["sel_len"], d["n_ctx"]))
+    ref = oracle.attention_of(d, rows=rows)
+    got = out if rows is None else out[rows]
+    H.assert_close(got, ref, what)
+    return out
+
+
+def test_attention_dense_workload_all_rows():
+    w = synth.workload(0)
+    print("case", w.name, flush=True)
+    _check_problem(synth.as_problem(synth.generate(w)), what=w.name)
+
+
+@pytest.mark.parametrize("idx,n_groups", [(1, 24), (2, 12), (3, 12), (4, 12)])
+def test_attention_workloads_sampled_groups(idx, n_groups):
+    """Full-size inputs in the benchmark's launch configuration; whole sampled groups."""
+    w = synth.workload(idx)
+    print("case", w.name, flush=True)
+    d = synth.as_problem(synth.generate(w))
+    rows = H.sample_rows(w.n_q, n_groups, seed=idx)
+    out = _check_problem(d, rows=rows, what=w.name)
+    assert np.all(np.isfinite(out))
+    # a property that holds for every output: a convex combination of V rows
+    vmax = float(np.abs(d["v_pool"].astype(np.float32) * d["v_scale"][..., None]).max())
+    assert float(np.abs(out).max()) <= vmax * (1 + 1e-2)
+
+
+@pytest.mark.parametrize("seed,n_ctx,n_q,n_kv,dup,nonres", [
+    (21, 1000, 45, 2, 0.3, 0.3), (22, 3000, 64, 1, 0.0, 0.5), (23, 700, 13, 3, 0.5, 0.0),
+    (24, 4100, 9, 4, 0.2, 0.1)])
+def test_attention_random_selections_all_rows(seed, n_ctx, n_q, n_kv, dup, nonres):
+    print("case", seed, n_ctx, n_q, n_kv, flush=True)
+    d = synth.small_random(seed, n_ctx=n_ctx, n_q=n_q, n_kv=n_kv, dup_frac=dup,
+                           nonresident_frac=nonres, pool_extra=2)
+    out = _check_problem(d, what="random seed %d" % seed)
+    empty = d["sel_len"] == 0
+    assert np.all(out[empty] == 0)
+
+
+def test_attention_exact_mean_catches_single_cell_errors():
+    """K = 0 and v_scale = 2^-6: every probability is exactly 1 in FP16, sums are
+    exact in FP32, so the output is 2^-6 * mean(v_int over the resident set) to
+    within 2 ulp. Dropping or adding one cell of ~2,000 would move it far more."""
+    w = synth.workload(2)
+    print("case exact mean", w.name, flush=True)
+    d = synth.as_problem(synth.generate(w))
+    d["k_pool"] = np.zeros_like(d["k_pool"])
+    d["v_scale"] = np.full_like(d["v_scale"], np.float32(2.0 ** -6))
+    pt = d["page_table"].copy()
+    pt[[3, 100, 257, 511]] = -1               # some pages not resident
+    d["page_table"] = pt
+    dev = H.to_device(d)
+    out, cells, mask, length, status = H.run_path(d, dev)
+    assert status == 0
+    rows = H.sample_rows(w.n_q, 16, seed=7)
+    # closed form in integer arithmetic: 2^-6 * sum(v_int) / |R_j|
+    ref = np.zeros((rows.size, w.n_qh, w.head_dim))
+    for r, j in enumerate(rows):
+        cells = np.unique(d["sel"][j, :d["sel_len"][j]])
+        pp = pt[cells // 64]
+        cells, pp = cells[pp >= 0], pp[pp >= 0]
+        for kv in range(w.n_kv):
+            tot = d["v_pool"][pp, kv, cells % 64, :].astype(np.int64).sum(axis=0)
+            ref[r, kv * 12:(kv + 1) * 12] = (tot / cells.size) * 2.0 ** -6
+    got = out[rows].astype(np.float64)
+    tol = 2 * np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (np.argwhere(bad)[:5], got[bad][:5], ref[bad][:5])
+    # the oracle agrees with the closed form
+    assert np.max(np.abs(oracle.attention_of(d, rows=rows[:8]) - ref[:8])) <= 1e-15
+
+
+def test_attention_bitwise_rerun_and_row_order():
+    w = synth.workload(3)            # shuffled rows
+    print("case rerun", w.name, flush=True)
+    d = synth.as_problem(synth.generate(w))
+    dev = H.to_device(d)
+    out1 = H.run_path(d, dev)[0]
+    out2 = H.run_path(d, dev)[0]
+    assert np.array_equal(out1.view(np.uint32), out2.view(np.uint32))
+    # sorting every selection row changes nothing (the union is a set)
+    s = d["sel"].copy()
+    for j in range(w.n_q):
+        s[j, :d["sel_len"][j]] = np.sort(s[j, :d["sel_len"][j]])
+    e = dict(d)
+    e["sel"] = s
+    out3 = H.run_path(e)[0]
+    assert np.array_equal(out1.view(np.uint32), out3.view(np.uint32))
+
+
+def test_attention_flags_data_errors():
+    d = synth.small_random(31, n_ctx=640, n_q=16, n_kv=1)
+    dev = H.to_device(d)
+    cells, mask, length, status = sa.build_union(dev["sel"], dev["sel_len"], 640)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    # a page-table entry past the pool and a too-large v_scale
+    pt = dev["page_table"].clone()
+    pt[2] = d["n_pages"] + 5
+    vs = dev["v_scale"].clone()
+    vs[int(d["page_table"][0])] = 8.0
+    out, st = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], vs, pt, cells,
+                         mask, length, float(d["softmax_scale"]), 640)
+    torch.cuda.synchronize()
+    v = int(st.item())
+    assert v & sa.STATUS_PAGE_RANGE and v & sa.STATUS_V_SCALE
+    # a union length over the capacity is clamped and flagged
+    bad_len = length.clone()
+    bad_len[0] = cells.shape[1] + 1
+    out, st = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
+                         dev["v_scale"], dev["page_table"], cells, mask, bad_len,
+                         float(d["softmax_scale"]), 640)
+    torch.cuda.synchronize()
+    assert int(st.item()) & sa.STATUS_UNION_LEN
