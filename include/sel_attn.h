@@ -78,7 +78,8 @@ typedef struct sel_attn_dims {
   int32_t page_size; /* cells per page; must be 64 */
   int32_t sel_cap;   /* row stride of sel, >= 1 (2051 in the headline workloads);
                         each group's union rows have stride 8 * sel_cap */
-  int32_t n_pages;   /* physical pages in each pool, >= 1 */
+  int32_t n_pages;   /* physical pages in each pool, >= 1; a pool
+                        (n_pages * n_kv * 64 * 128 bytes) must stay under 4 GiB */
 } sel_attn_dims;
 
 /*

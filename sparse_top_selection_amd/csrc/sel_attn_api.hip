@@ -52,10 +52,10 @@ int check_dims(const sel_attn_dims* d, const char* who) {
   // union rows of 8*sel_cap int32 cells: the per-group length must fit an int32
   if ((int64_t)d->sel_cap * 8 > INT32_MAX)
     return fail(SEL_ATTN_EINVAL, "%s: sel_cap %d too large", who, d->sel_cap);
-  // pool rows are indexed as int32 (phys * n_kv + h) * 64 + slot
-  if ((int64_t)d->n_pages * d->n_kv * SEL_ATTN_PAGE_SIZE > INT32_MAX)
-    return fail(SEL_ATTN_EINVAL, "%s: pool of %d pages x %d KV heads too large", who, d->n_pages,
-                d->n_kv);
+  // pool rows are addressed with 32-bit byte offsets: each pool stays under 4 GiB
+  if ((int64_t)d->n_pages * d->n_kv * SEL_ATTN_PAGE_SIZE * SEL_ATTN_HEAD_DIM > (int64_t)UINT32_MAX)
+    return fail(SEL_ATTN_EINVAL, "%s: pool of %d pages x %d KV heads exceeds 4 GiB", who,
+                d->n_pages, d->n_kv);
   if ((int64_t)d->n_kv * SEL_ATTN_Q_PER_KV * ((int64_t)(d->n_q + 7) / 8) > INT32_MAX)
     return fail(SEL_ATTN_EINVAL, "%s: n_q x n_kv too large", who);
   return SEL_ATTN_OK;

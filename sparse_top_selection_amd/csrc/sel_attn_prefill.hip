@@ -11,16 +11,24 @@
 //
 // gfx950 mapping (the page's 16-lane sub-group / 256-GRF shape is Xe2 prior art
 // and is not reproduced):
-//   * one 384-thread workgroup (6 wave64s) per (group g, KV head h); grid order
-//     is XCD-aware so that each XCD walks consecutive groups of one KV head;
+//   * one 512-thread workgroup (8 wave64s, one per CU at this register budget,
+//     two per SIMD) per (group g, KV head h); grid order is XCD-aware so that
+//     each XCD walks consecutive groups of one KV head;
+//   * waves 0..5 consume, waves 6..7 produce. The producers translate union
+//     cells through the page table, gather the INT8 K/V rows with 16-byte /
+//     8-byte loads two chunks ahead of their use, convert them to FP16 and store
+//     them into a 4-stage LDS ring of tiles; the consumers only read LDS;
 //   * row n of the 96 = 8*hq + i (query head h*12+hq, position 8g+i), so the
-//     chooser bit of row n is n & 7; wave w owns row block rb = w % 3 (32 rows)
-//     and cell half ch = w / 3 (32 of the chunk's 64 cells) with its own softmax
-//     state; the two halves are merged once at the end;
-//   * S^T (32 cells x 32 rows, K=128) is 8 v_mfma_f32_32x32x16_f16 from an LDS K
-//     tile and Q^T held in registers; O^T (128 dims x 32 rows) += V^T P^T is 8
+//     chooser bit of row n is n & 7; consumer wave w owns row block rb = w % 3
+//     (32 rows) and cell half ch = w / 3 (32 of each chunk's 64 cells) with its
+//     own softmax state; the two halves are merged once at the end;
+//   * S^T (32 cells x 32 rows, K=128) is 8 v_mfma_f32_32x32x16_f16 from the LDS K
+//     tile with Q^T held in registers; O^T (128 dims x 32 rows) += V^T P^T is 8
 //     more MFMAs whose B operand (P^T) comes straight from the S^T accumulator
-//     registers: the V^T tile in LDS is stored in the matching cell permutation;
+//     registers: the V^T tile is stored in the matching cell permutation;
+//   * each consumer iteration issues the MFMAs of S^T for chunk c+1 and of
+//     O^T += V^T P^T for chunk c-1, interleaved with the softmax of chunk c, so
+//     the matrix pipe and the VALU work at the same time;
 //   * K and V integers are exact in FP16, so the scales are applied in FP32:
 //     k_scale * softmax_scale * log2(e) multiplies the score, v_scale * 2^10 the
 //     probability before its FP16 rounding (2^-10 returns in the epilogue);
@@ -29,11 +37,7 @@
 //   * online softmax with a lazy stabiliser: probabilities are taken against
 //     the running maximum, and only when a lane's chunk sum exceeds 16 does the
 //     wave recompute the chunk maximum and rescale O and l (always on a row's
-//     first chosen chunk, rarely after);
-//   * a chunk's INT8 K/V are gathered through the page table with 16-byte loads
-//     one chunk ahead (and the page translation two chunks ahead), converted
-//     to FP16 in registers (byte permute + magic-number subtract, V transposed
-//     4x4 on the way) and written to the other half of a double-buffered tile.
+//     first chosen chunk, rarely after).
 
 #include "sel_attn_internal.h"
 
@@ -46,35 +50,49 @@ typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 6;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 64;        // union cells per iteration
-constexpr int kD = 128;           // head dim
+constexpr int kConsumerWaves = 6;   // 3 row blocks x 2 cell halves
+constexpr int kProducerWaves = 2;   // translate, gather, convert
+constexpr int kThreads = 64 * (kConsumerWaves + kProducerWaves);
+constexpr int kChunk = 64;          // union cells per iteration
+constexpr int kD = 128;             // head dim
 constexpr int kQPerKv = 12;
+constexpr int kStages = 4;          // LDS tiles: chunks c-1 (V), c, c+1 (K), c+2 (being written)
+constexpr int kRing = 4;            // translated chunks c+2 .. c+4
 constexpr float kLazyLimit = 16.f;
-constexpr float kNoMax = -1e30f;  // stabiliser before a row has seen a chosen cell
-constexpr float kVFold = 1024.f;  // probabilities carry v_scale * 2^10 into FP16
+constexpr float kNoMax = -1e30f;    // stabiliser before a row has seen a chosen cell
+constexpr float kVFold = 1024.f;    // probabilities carry v_scale * 2^10 into FP16
 constexpr float kVScaleLimit = 4.f;
 
 struct __align__(16) Stage {
-  _Float16 k[kChunk * kD];   // [cell][dim]; 16-byte unit u of a row stored at u ^ (cell & 15)
-  _Float16 vt[kD * kChunk];  // [dim][slot]; 16-byte unit w of a row stored at w ^ (dim & 7)
-  float kf[kChunk];          // k_scale * softmax_scale * log2(e); 0 where unusable
-  float vf[kChunk];          // v_scale * 2^10; 0 where unusable
+  _Float16 k[kChunk * kD];     // [cell][dim], swizzled by k_unit()
+  _Float16 vt[kD * kChunk];    // [dim][slot], swizzled by v_unit()
+  float kf[kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
+  float vf[kChunk];            // v_scale * 2^10; 0 where unusable
   uint32_t emask[kChunk / 4];  // chooser bytes, 0 for padding / non-resident cells
+  uint32_t emask_spare[kChunk / 4];  // written by the producer wave that owns vf
 };
 
 struct Ring {
-  int32_t row[kChunk];       // pool row (phys * n_kv + h) * 64 + slot; -1 = unusable
+  int32_t row[kChunk];         // pool row (phys * n_kv + h) * 64 + slot; -1 = unusable
   uint8_t mask[kChunk];
 };
 
 struct __align__(16) Smem {
-  Stage st[2];
-  Ring ring[2];
+  Stage st[kStages];
+  Ring ring[kRing + 1];   // the last slot takes the second producer wave's copy
 };
+
+// ---------------------------------------------------------------------------
+// Workgroup barrier that orders LDS only. Threads of a workgroup talk to each
+// other through LDS alone (global memory is only read, plus the output stores
+// and the status atomic), so the barrier need not wait for outstanding global
+// loads: the producers' gathers stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---------------------------------------------------------------------------
 // INT8 -> FP16: bias each byte to unsigned (v + 128), place it under the FP16
@@ -93,14 +111,43 @@ __device__ __forceinline__ half4 i8x4_to_half4(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------
-// Staging tasks. K task t in [0,512): cell t>>3, dims 16*(t&7)..+15 (one 16-byte
-// load). V task t in [0,512): cells 4*(t>>5)..+3, dims 4*(t&31)..+3 (four dword
-// loads, transposed to four dims x four cells).
+// LDS tile layouts. Both are XOR-swizzled in 16-byte units so that the
+// producers' stores and the consumers' MFMA-operand loads are free of bank
+// conflicts (8 consecutive lanes always touch 8 distinct units of a 128-byte
+// bank period).
+//
+// K tile [cell][dim], 16 units of 8 dims per cell row. Unit u (dims 8u..8u+7)
+// of cell c lives at rot(u) ^ (c & 15), rot(u) = ((u & 1) << 3) | (u >> 1).
+// Consumers load unit 2ks+hb of 8 consecutive cells; producers store units 2p
+// and 2p+1 (p = 0..7) of one cell.
+__device__ __forceinline__ int k_unit(int u, int cell) {
+  return (((u & 1) << 3) | (u >> 1)) ^ (cell & 15);
+}
+
+// V^T tile [dim][slot], 8 units of 8 cells per dim row. Unit w = 4ch + 2ks + hb
+// holds cells 16(2ch+ks) + 4hb + {0..3} then the same + 8: the order in which a
+// lane of the S^T accumulator holds its cells, so P^T feeds the PV MFMA from
+// registers. Unit w of dim d lives at w ^ vswz(d), vswz(d) = (d ^ (d >> 3)) & 7.
+// Consumers load unit w of 8 consecutive dims; producers store unit w of dims
+// 8k + jd for 8 consecutive k.
+__device__ __forceinline__ int v_unit(int w, int d) { return w ^ ((d ^ (d >> 3)) & 7); }
+
+// first cell of the k-th 4-cell quad (k = 0, 1) held by V^T unit w
+__device__ __forceinline__ int v_unit_cell(int w, int k) {
+  return 16 * (w >> 1) + 4 * (w & 1) + 8 * k;
+}
+
+// ---------------------------------------------------------------------------
+// Producer staging tasks. K task t in [0,512): cell t>>3, dims 16*(t&7)..+15 (one
+// 16-byte load). V task t in [0,128): unit w = t>>4 (eight cells), dims
+// 8*(t&15)..+7 (eight 8-byte loads, transposed to eight dims x eight cells).
+// Unusable cells (padding, non-resident, bad) read pool row 0, which always
+// exists; their chooser byte and scales are 0, so the values never count.
+__device__ __forceinline__ uint32_t row_bytes(int row) { return (uint32_t)max(row, 0) * kD; }
+
 __device__ __forceinline__ u32x4 load_k_task(const PrefillArgs& a, const Ring& rg, int t) {
-  const int row = rg.row[t >> 3];
-  if (row < 0) return u32x4{0u, 0u, 0u, 0u};
-  const u32x4* p = reinterpret_cast<const u32x4*>(a.k_pool + (int64_t)row * kD + 16 * (t & 7));
-  return *p;
+  const uint32_t off = row_bytes(rg.row[t >> 3]) + 16u * (t & 7);
+  return *reinterpret_cast<const u32x4*>(a.k_pool + off);
 }
 
 __device__ __forceinline__ void store_k_task(Stage& st, int t, u32x4 raw) {
@@ -111,38 +158,41 @@ __device__ __forceinline__ void store_k_task(Stage& st, int t, u32x4 raw) {
   const half8 a0 = half8{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
   const half8 a1 = half8{h2.x, h2.y, h2.z, h2.w, h3.x, h3.y, h3.z, h3.w};
   _Float16* base = st.k + cell * kD;
-  *reinterpret_cast<half8*>(base + ((u0 ^ (cell & 15)) << 3)) = a0;
-  *reinterpret_cast<half8*>(base + (((u0 + 1) ^ (cell & 15)) << 3)) = a1;
+  *reinterpret_cast<half8*>(base + (k_unit(u0, cell) << 3)) = a0;
+  *reinterpret_cast<half8*>(base + (k_unit(u0 + 1, cell) << 3)) = a1;
 }
 
-__device__ __forceinline__ u32x4 load_v_task(const PrefillArgs& a, const Ring& rg, int t) {
-  const int c0 = 4 * (t >> 5);
-  const int dq = t & 31;
-  u32x4 r;
+struct VRaw {
+  u32x4 lo0, lo1;   // dims 8dq..8dq+3 of the unit's first / second cell quad
+  u32x4 hi0, hi1;   // dims 8dq+4..8dq+7
+};
+
+__device__ __forceinline__ VRaw load_v_task(const PrefillArgs& a, const Ring& rg, int t) {
+  const int w = t >> 4;
+  const uint32_t d8 = 8u * (t & 15);
+  VRaw r;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int row = rg.row[c0 + k];
-    uint32_t w = 0u;
-    if (row >= 0)
-      w = reinterpret_cast<const uint32_t*>(a.v_pool + (int64_t)row * kD)[dq];
-    r[k] = w;
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t off = row_bytes(rg.row[v_unit_cell(w, k >> 2) + (k & 3)]) + d8;
+    const uint2 x = *reinterpret_cast<const uint2*>(a.v_pool + off);
+    if (k < 4) {
+      r.lo0[k] = x.x;
+      r.hi0[k] = x.y;
+    } else {
+      r.lo1[k - 4] = x.x;
+      r.hi1[k - 4] = x.y;
+    }
   }
   return r;
 }
 
-// V^T slot layout: within a row (one dim), 16-byte unit w = 4*ch + 2*ks + hb
-// holds cells 32ch + 16ks + 4hb + {0..3} then 32ch + 16ks + 8 + 4hb + {0..3},
-// which is the order in which an S^T accumulator lane holds its cells.
-__device__ __forceinline__ void store_v_task(Stage& st, int t, u32x4 raw) {
-  const int c0 = 4 * (t >> 5);     // first of four consecutive cells
-  const int d0 = 4 * (t & 31);
-  const int w = ((c0 >> 5) << 2) | (((c0 >> 4) & 1) << 1) | ((c0 >> 2) & 1);
-  const int sub = ((c0 >> 3) & 1) << 2;   // first or second half of the unit
-  // 4x4 byte transpose: t01 = cells 0,1 interleaved, t23 = cells 2,3 interleaved
+// four int8 dwords (cells 0..3, bytes = dims 0..3) -> for each dim jd the four
+// cells' halves, via a 4x4 byte transpose and the biased FP16 trick.
+__device__ __forceinline__ void transpose_quad(u32x4 raw, half4 out[4]) {
   const uint32_t w0 = raw.x ^ 0x80808080u, w1 = raw.y ^ 0x80808080u;
   const uint32_t w2 = raw.z ^ 0x80808080u, w3 = raw.w ^ 0x80808080u;
-  const uint32_t t01lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
-  const uint32_t t01hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+  const uint32_t t01lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // c0d0 c1d0 c0d1 c1d1
+  const uint32_t t01hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // c0d2 c1d2 c0d3 c1d3
   const uint32_t t23lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
   const uint32_t t23hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
   const uint32_t src01[2] = {t01lo, t01hi};
@@ -152,78 +202,114 @@ __device__ __forceinline__ void store_v_task(Stage& st, int t, u32x4 raw) {
     const uint32_t sel = (jd & 1) ? 0x04030402u : 0x04010400u;
     const half2 a01 = biased_pair_to_half2(__builtin_amdgcn_perm(0x64646464u, src01[jd >> 1], sel));
     const half2 a23 = biased_pair_to_half2(__builtin_amdgcn_perm(0x64646464u, src23[jd >> 1], sel));
+    out[jd] = half4{a01.x, a01.y, a23.x, a23.y};
+  }
+}
+
+__device__ __forceinline__ void store_v_task(Stage& st, int t, const VRaw& raw) {
+  const int w = t >> 4;
+  const int d0 = 8 * (t & 15);
+  half4 a0[4], a1[4], b0[4], b1[4];
+  transpose_quad(raw.lo0, a0);
+  transpose_quad(raw.lo1, a1);
+  transpose_quad(raw.hi0, b0);
+  transpose_quad(raw.hi1, b1);
+#pragma unroll
+  for (int jd = 0; jd < 4; ++jd) {
     const int d = d0 + jd;
-    *reinterpret_cast<half4*>(st.vt + d * kChunk + ((w ^ (d & 7)) << 3) + sub) =
-        half4{a01.x, a01.y, a23.x, a23.y};
+    *reinterpret_cast<half8*>(st.vt + d * kChunk + (v_unit(w, d) << 3)) =
+        half8{a0[jd].x, a0[jd].y, a0[jd].z, a0[jd].w, a1[jd].x, a1[jd].y, a1[jd].z, a1[jd].w};
+    const int e = d0 + 4 + jd;
+    *reinterpret_cast<half8*>(st.vt + e * kChunk + (v_unit(w, e) << 3)) =
+        half8{b0[jd].x, b0[jd].y, b0[jd].z, b0[jd].w, b1[jd].x, b1[jd].y, b1[jd].z, b1[jd].w};
   }
-}
-
-// Page translation for chunk cc, split in two so the union read overlaps work.
-struct Pending {
-  int32_t cell;
-  uint32_t mask;
-  bool valid;
-};
-
-__device__ __forceinline__ Pending translate_issue(const PrefillArgs& a, int64_t ubase, int U,
-                                                   int cc, int tid) {
-  Pending p{0, 0u, false};
-  const int idx = cc * kChunk + tid;
-  if (idx < U) {
-    p.cell = a.union_cells[ubase + idx];
-    p.mask = a.union_mask[ubase + idx];
-    p.valid = true;
-  }
-  return p;
-}
-
-__device__ __forceinline__ void translate_finish(const PrefillArgs& a, const Pending& p, int h,
-                                                 Ring& rg, int tid, uint32_t& flags) {
-  int32_t row = -1;
-  if (p.valid) {
-    if (p.cell < 0 || p.cell >= a.n_ctx) {
-      flags |= SEL_ATTN_STATUS_CELL_RANGE;
-    } else {
-      const int32_t pp = a.page_table[p.cell >> 6];
-      if (pp >= a.n_pages || pp < -1) {
-        flags |= SEL_ATTN_STATUS_PAGE_RANGE;
-      } else if (pp >= 0) {
-        row = (pp * a.n_kv + h) * 64 + (p.cell & 63);
-      }
-    }
-  }
-  rg.row[tid] = row;
-  rg.mask[tid] = (row >= 0) ? (uint8_t)p.mask : (uint8_t)0;
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs a) {
-  __shared__ Smem sm;
+// Page translation of one chunk cell (producer wave 6, one lane per cell), in
+// three steps spread over two iterations so that no global read sits on the
+// critical path: read the union entry, then the page-table entry, then form
+// the pool row.
+struct Pending {
+  int32_t cell;
+  uint8_t mask;
+  int32_t page;    // page-table entry, once read
+  bool valid;
+};
 
-  const int b = blockIdx.x;
-  const int L = (b & 7) * a.per_xcd + (b >> 3);
-  if (L >= a.n_groups * a.n_kv) return;
-  const int h = L / a.n_groups;
-  const int g = L - h * a.n_groups;
+// All three steps are branch-free (clamped, always-valid addresses plus selects)
+// so that a producer iteration stays one basic block and the compiler's memory
+// waits can let a chunk's loads run across the barrier into the next iteration.
+__device__ __forceinline__ Pending read_union_entry(const PrefillArgs& a, int64_t ubase, int U,
+                                                    int cc, int lane) {
+  // union rows hold at least 8 entries, so index 0 is always readable
+  const int idx = cc * kChunk + lane;
+  const bool valid = idx < U;
+  const int64_t at = ubase + (valid ? idx : 0);
+  Pending p;
+  p.cell = a.union_cells[at];
+  p.mask = a.union_mask[at];
+  p.page = -1;
+  p.valid = valid;
+  return p;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int rb = wave % 3;          // row block: rows 32rb..32rb+31
-  const int ch = wave / 3;          // cell half of every chunk
-  const int hb = lane >> 5;         // which half of the wave
+__device__ __forceinline__ void read_page_entry(const PrefillArgs& a, Pending& p) {
+  const bool in_ctx = p.valid && p.cell >= 0 && p.cell < a.n_ctx;
+  const int32_t e = a.page_table[in_ctx ? (p.cell >> 6) : 0];
+  p.page = in_ctx ? e : -1;
+}
+
+__device__ __forceinline__ void finish_translation(const PrefillArgs& a, const Pending& p, int h,
+                                                   Ring& rg, int lane, uint32_t& flags) {
+  const bool cell_bad = p.valid && (p.cell < 0 || p.cell >= a.n_ctx);
+  const bool page_bad = p.valid && !cell_bad && (p.page >= a.n_pages || p.page < -1);
+  flags |= (cell_bad ? SEL_ATTN_STATUS_CELL_RANGE : 0u) | (page_bad ? SEL_ATTN_STATUS_PAGE_RANGE : 0u);
+  const bool usable = p.valid && !cell_bad && !page_bad && p.page >= 0;
+  const int32_t row = usable ? (p.page * a.n_kv + h) * 64 + (p.cell & 63) : -1;
+  rg.row[lane] = row;
+  rg.mask[lane] = usable ? p.mask : (uint8_t)0;
+}
+
+// ---------------------------------------------------------------------------
+// Consumer waves 0..5: row block rb = w % 3 (32 rows), cell half ch = w / 3.
+__device__ __forceinline__ float16v scores_t(const Stage& st, const half8 qf[8], int ch, int hb,
+                                             int l32) {
+  float16v s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  const int cell = 32 * ch + l32;
+  const _Float16* krow = st.k + cell * kD;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const half8 ka = *reinterpret_cast<const half8*>(krow + (k_unit(2 * ks + hb, cell) << 3));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// O^T (128 dims x 32 rows) += V^T (dims x this wave's 32 cells) P'^T
+__device__ __forceinline__ void pv_accumulate(const Stage& st, const half8 pb[2], float16v o[4],
+                                              int ch, int hb, int l32) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int d = 32 * mb + l32;
+      const int w = 4 * ch + 2 * ks + hb;
+      const half8 va = *reinterpret_cast<const half8*>(st.vt + d * kChunk + (v_unit(w, d) << 3));
+      o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[ks], o[mb], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
+                                        int nch_even, int wave, int lane) {
+  const int rb = wave % 3;
+  const int ch = wave / 3;
+  const int hb = lane >> 5;
   const int l32 = lane & 31;
   const int n_qh = a.n_kv * kQPerKv;
-  const int64_t ucap = 8LL * a.sel_cap;
-  const int64_t ubase = (int64_t)g * ucap;
-  uint32_t flags = 0;
-
-  int U = a.union_len[g];
-  if (U < 0 || U > ucap) {
-    flags |= SEL_ATTN_STATUS_UNION_LEN;
-    U = U < 0 ? 0 : (int)ucap;
-  }
-  const int nch = (U + kChunk - 1) / kChunk;
 
   // this lane's row: query head h*12 + hq, query index 8g + i
   const int row_n = 32 * rb + l32;
@@ -238,67 +324,16 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
     const float* qrow = a.q + ((int64_t)(row_ok ? qi : 0) * n_qh + h * kQPerKv + hq) * kD;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      float4v x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-      if (row_ok) {
-        x0 = *reinterpret_cast<const float4v*>(qrow + 16 * s + 8 * hb);
-        x1 = *reinterpret_cast<const float4v*>(qrow + 16 * s + 8 * hb + 4);
-      }
+      float4v x0 = *reinterpret_cast<const float4v*>(qrow + 16 * s + 8 * hb);
+      float4v x1 = *reinterpret_cast<const float4v*>(qrow + 16 * s + 8 * hb + 4);
+      if (!row_ok) x0 = x1 = float4v{0.f, 0.f, 0.f, 0.f};
       qf[s] = half8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
                     (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
     }
   }
 
-  // staging task ids of this thread
-  const int kA = tid;
-  const int kB = tid + kThreads;            // valid for tid < 128
-  const int vA = tid - 128;                 // valid for tid >= 128
-  const int vB = tid + 256;                 // valid for tid < 256
-
-  // prologue: translate chunks 0 and 1, stage chunk 0
-  if (tid < kChunk) {
-    Pending p0 = translate_issue(a, ubase, U, 0, tid);
-    Pending p1 = translate_issue(a, ubase, U, 1, tid);
-    translate_finish(a, p0, h, sm.ring[0], tid, flags);
-    translate_finish(a, p1, h, sm.ring[1], tid, flags);
-  }
-  __syncthreads();
-
-  u32x4 rkA, rkB, rvA, rvB;
-  float sc = 0.f;
-  auto issue_loads = [&](const Ring& rg) {
-    rkA = load_k_task(a, rg, kA);
-    if (tid < 128) rkB = load_k_task(a, rg, kB);
-    if (tid >= 128) rvA = load_v_task(a, rg, vA);
-    if (tid < 256) rvB = load_v_task(a, rg, vB);
-    sc = 0.f;
-    if (tid < 2 * kChunk) {
-      const int row = rg.row[tid & 63];
-      if (row >= 0) sc = (tid < kChunk) ? a.k_scale[row] : a.v_scale[row];
-    }
-  };
-  auto finish_stage = [&](Stage& st, const Ring& rg) {
-    store_k_task(st, kA, rkA);
-    if (tid < 128) store_k_task(st, kB, rkB);
-    if (tid >= 128) store_v_task(st, vA, rvA);
-    if (tid < 256) store_v_task(st, vB, rvB);
-    if (tid < kChunk) {
-      st.kf[tid] = sc * a.score_scale;
-      reinterpret_cast<uint8_t*>(st.emask)[tid] = rg.mask[tid];
-    } else if (tid < 2 * kChunk) {
-      float vf = sc * kVFold;
-      if (!(fabsf(sc) < kVScaleLimit)) {
-        flags |= SEL_ATTN_STATUS_V_SCALE;
-        vf = 0.f;
-      }
-      st.vf[tid - kChunk] = vf;
-    }
-  };
-
-  if (nch > 0) {
-    issue_loads(sm.ring[0]);
-    finish_stage(sm.st[0], sm.ring[0]);
-  }
-  __syncthreads();
+  lds_barrier();   // prologue: ring filled
+  lds_barrier();   // prologue: chunks 0 and 1 staged, stage 3's V^T zeroed
 
   // running softmax state of this lane's row (over this wave's cell half)
   float m_run = kNoMax;
@@ -308,33 +343,37 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
-
   const float ninf = -__builtin_inff();
 
-  for (int c = 0; c < nch; ++c) {
-    const Stage& st = sm.st[c & 1];
-    Pending nx{0, 0u, false};
-    if (c + 2 < nch && tid < kChunk) nx = translate_issue(a, ubase, U, c + 2, tid);
-    if (c + 1 < nch) issue_loads(sm.ring[(c + 1) & 1]);
-
-    // ---- S^T = K Q^T for cells 32ch..32ch+31 of the chunk
-    float16v s;
+  // Software pipeline: iteration c issues the MFMAs of S^T(c+1) and of
+  // O^T += V^T P^T for chunk c-1 (whose P^T is already in registers), then runs
+  // the softmax of chunk c on the VALU while those MFMAs execute. The first
+  // iteration multiplies a zeroed P^T with stage 3's V^T (zero-filled by the
+  // producers); the last one computes a discarded S^T.
+  float16v s_cur = scores_t(sm.st[0], qf, ch, hb, l32);
+  half8 pb[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    {
-      const int cell = 32 * ch + l32;
-      const _Float16* krow = st.k + cell * kD;
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const half8 ka = *reinterpret_cast<const half8*>(krow + (((2 * ks + hb) ^ (cell & 15)) << 3));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], s, 0, 0, 0);
-      }
-    }
+    for (int e = 0; e < 8; ++e) pb[ks][e] = (_Float16)0.f;
 
-    // ---- chooser masks (wave-uniform) and per-cell factors
+  for (int c = 0; c < nch_even; ++c) {
+    const Stage& st = sm.st[c % kStages];
+    const Stage& st_prev = sm.st[(c + kStages - 1) % kStages];
+
+    // ---- matrix work that does not wait for this chunk's softmax
+    const float16v s_next = scores_t(sm.st[(c + 1) % kStages], qf, ch, hb, l32);
+    pv_accumulate(st_prev, pb, o, ch, hb, l32);
+
+    // ---- chooser masks (wave-uniform) and per-cell factors of chunk c
+    const u32x4 em_lo = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch);
+    const u32x4 em_hi = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch + 4);
     uint32_t em[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) em[k] = __builtin_amdgcn_readfirstlane(st.emask[8 * ch + k]);
+    for (int k = 0; k < 4; ++k) {
+      em[k] = __builtin_amdgcn_readfirstlane(em_lo[k]);
+      em[4 + k] = __builtin_amdgcn_readfirstlane(em_hi[k]);
+    }
     float kf[16], vf[16];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -355,19 +394,33 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
       keep[r] = __builtin_amdgcn_inverse_ballot_w64(lm);
     }
 
-    // ---- masked online softmax (log2 domain)
+    // ---- masked online softmax of chunk c (log2 domain), P'^T into pb
     float p[16];
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float u = keep[r] ? __builtin_fmaf(s[r], kf[r], -m_run) : ninf;
+      const float u = keep[r] ? __builtin_fmaf(s_cur[r], kf[r], -m_run) : ninf;
       p[r] = __builtin_amdgcn_exp2f(u);
       psum += p[r];
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (_Float16)(p[r] * vf[r]);
+
+    // interleave: one MFMA, then a few VALU / LDS-read instructions
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);   // VALU incl. transcendental
+      __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);   // SALU
+    }
+
     if (__ballot(!(psum <= kLazyLimit))) {
+      // the running maximum moves: rescale what is accumulated (this waits
+      // for the MFMAs issued above) and redo the chunk against the new maximum
       float cmax = ninf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) cmax = fmaxf(cmax, keep[r] ? s[r] * kf[r] : ninf);
+      for (int r = 0; r < 16; ++r) cmax = fmaxf(cmax, keep[r] ? s_cur[r] * kf[r] : ninf);
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
       const float m_new = fmaxf(m_run, cmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -380,32 +433,20 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
       psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float u = keep[r] ? __builtin_fmaf(s[r], kf[r], -m_run) : ninf;
+        const float u = keep[r] ? __builtin_fmaf(s_cur[r], kf[r], -m_run) : ninf;
         p[r] = __builtin_amdgcn_exp2f(u);
         psum += p[r];
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (_Float16)(p[r] * vf[r]);
     }
     l_run += psum;
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      half8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (_Float16)(p[8 * ks + e] * vf[8 * ks + e]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int d = 32 * mb + l32;
-        const int w = 4 * ch + 2 * ks + hb;
-        const half8 va = *reinterpret_cast<const half8*>(st.vt + d * kChunk + ((w ^ (d & 7)) << 3));
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[mb], 0, 0, 0);
-      }
-    }
-
-    if (c + 2 < nch && tid < kChunk) translate_finish(a, nx, h, sm.ring[c & 1], tid, flags);
-    if (c + 1 < nch) finish_stage(sm.st[(c + 1) & 1], sm.ring[(c + 1) & 1]);
-    __syncthreads();
+    s_cur = s_next;
+    lds_barrier();
   }
+  // the last chunk's P'^T
+  if (nch_even > 0) pv_accumulate(sm.st[(nch_even - 1) % kStages], pb, o, ch, hb, l32);
+  lds_barrier();   // every wave is done with the tiles the merge reuses
 
   // ---- merge the two cell halves of each row block and write the output
   float* xo = reinterpret_cast<float*>(&sm.st[0]);   // [3][16 float4 groups][64 lanes][4]
@@ -422,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
     xm[rb * 64 + lane] = m_run;
     xl[rb * 64 + lane] = l_run;
   }
-  __syncthreads();
+  lds_barrier();
   if (ch == 0) {
     const float m1 = xm[rb * 64 + lane];
     const float l1 = xl[rb * 64 + lane] + xl[rb * 64 + (lane ^ 32)];
@@ -438,13 +479,152 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4v o1 = *reinterpret_cast<const float4v*>(xo + ((rb * 16 + mb * 4 + q4) * 64 + lane) * 4);
+          const float4v o1 =
+              *reinterpret_cast<const float4v*>(xo + ((rb * 16 + mb * 4 + q4) * 64 + lane) * 4);
           float4v r;
 #pragma unroll
           for (int e = 0; e < 4; ++e) r[e] = (a0 * o[mb][4 * q4 + e] + a1 * o1[e]) * inv;
           *reinterpret_cast<float4v*>(orow + 32 * mb + 8 * q4 + 4 * hb) = r;
         }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Producer waves 6..7 (128 threads, ptid = tid - 384). Iteration c (while the
+// consumers work on chunks c and c+1): translate chunk c+4 (union entry read two
+// iterations earlier, page entry one), gather chunk c+3 into registers, convert
+// chunk c+2 (gathered one iteration earlier) into its LDS stage. Each thread
+// owns K tasks ptid + 128k (k = 0..3) and V task ptid, and
+// the k scale (ptid < 64) or v scale of cell ptid & 63; wave 6 translates.
+struct Raw {
+  u32x4 k[4];
+  VRaw v;
+  float sc;
+};
+
+__device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int ptid, Raw& r) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.k[k] = load_k_task(a, rg, ptid + 128 * k);
+  r.v = load_v_task(a, rg, ptid);
+  const int row = rg.row[ptid & 63];
+  const float* sp = (ptid < kChunk) ? a.k_scale : a.v_scale;
+  const float v = sp[max(row, 0)];
+  r.sc = row >= 0 ? v : 0.f;
+}
+
+__device__ __forceinline__ void convert(const PrefillArgs& a, Stage& st, const Ring& rg, int ptid,
+                                        const Raw& r, uint32_t& flags) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) store_k_task(st, ptid + 128 * k, r.k[k]);
+  store_v_task(st, ptid, r.v);
+  // wave 6 stores the k factors and chooser bytes, wave 7 the v factors (and
+  // a spare copy of the chooser bytes), without a branch
+  const bool kwave = ptid < kChunk;
+  const int lane = ptid & 63;
+  const bool v_ok = fabsf(r.sc) < kVScaleLimit;
+  flags |= (!kwave && !v_ok) ? SEL_ATTN_STATUS_V_SCALE : 0u;
+  const float f = kwave ? r.sc * a.score_scale : (v_ok ? r.sc * kVFold : 0.f);
+  (kwave ? st.kf : st.vf)[lane] = f;
+  reinterpret_cast<uint8_t*>(kwave ? st.emask : st.emask_spare)[lane] = rg.mask[lane];
+}
+
+__device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, int U,
+                                        int nch_even, int64_t ubase, int ptid, bool translator,
+                                        uint32_t& flags) {
+  // prologue: chunks 0..3 translated, page entry of chunk 4 read, union entry
+  // of chunk 5 read; chunks 0 and 1 staged, chunk 2 gathered. Both producer
+  // waves translate the same lanes; wave 7 writes its copy to the spare slot.
+  const int lane = ptid & 63;
+  auto ring_slot = [&](int cc) -> Ring& { return sm.ring[translator ? (cc % kRing) : kRing]; };
+  // Translation state alternates between two register sets so that every
+  // global read is consumed exactly one iteration after it was issued (no
+  // register copies of in-flight loads): a_* = union entry read, page entry
+  // next; b_* = page entry read, pool row next.
+  Pending a0, a1, b0, b1;
+  {
+    Pending p[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) p[i] = read_union_entry(a, ubase, U, i, lane);
+    b1 = read_union_entry(a, ubase, U, kRing, lane);
+    a1 = read_union_entry(a, ubase, U, kRing + 1, lane);
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) read_page_entry(a, p[i]);
+    read_page_entry(a, b1);
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) finish_translation(a, p[i], h, ring_slot(i), lane, flags);
+  }
+  // stage 3's V^T meets a zeroed P^T in the consumers' first iteration: keep
+  // it finite
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(sm.st[kStages - 1].vt);
+#pragma unroll
+    for (int i = 0; i < (kD * kChunk * 2) / (16 * 128); ++i) z[ptid + 128 * i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  lds_barrier();
+  Raw set0, set1;
+  gather(a, sm.ring[0], ptid, set0);
+  gather(a, sm.ring[1], ptid, set1);
+  convert(a, sm.st[0], sm.ring[0], ptid, set0, flags);
+  gather(a, sm.ring[2], ptid, set0);
+  convert(a, sm.st[1], sm.ring[1], ptid, set1, flags);
+  lds_barrier();
+
+  // Iteration c: gather chunk c+3 into one register set, finish the
+  // translation of chunk c+4, read the page entry of chunk c+5 and the union
+  // entry of chunk c+6, convert chunk c+2 from the other set. Chunks past the
+  // end are harmless: their ring rows are -1 (row 0 is read, masks and scales
+  // are 0) and their stages are never read for results.
+  auto step = [&](int c, Raw& load_set, Raw& conv_set, Pending& a_in, Pending& a_out,
+                  Pending& b_in, Pending& b_out) {
+    gather(a, sm.ring[(c + 3) % kRing], ptid, load_set);
+    finish_translation(a, b_in, h, ring_slot(c + 4), lane, flags);   // chunk c+4
+    b_out = a_in;
+    read_page_entry(a, b_out);                                         // chunk c+5
+    a_out = read_union_entry(a, ubase, U, c + 6, lane);                // chunk c+6
+    convert(a, sm.st[(c + 2) % kStages], sm.ring[(c + 2) % kRing], ptid, conv_set, flags);
+    lds_barrier();
+  };
+  for (int c = 0; c < nch_even; c += 2) {
+    step(c, set1, set0, a1, a0, b1, b0);
+    step(c + 1, set0, set1, a0, a1, b0, b1);
+  }
+  lds_barrier();   // consumers finish their last O^T update
+  lds_barrier();   // merge of the consumers' two cell halves
+}
+
+__global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs a) {
+  __shared__ Smem sm;
+
+  const int b = blockIdx.x;
+  const int L = (b & 7) * a.per_xcd + (b >> 3);
+  if (L >= a.n_groups * a.n_kv) return;
+  const int h = L / a.n_groups;
+  const int g = L - h * a.n_groups;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t ucap = 8LL * a.sel_cap;
+  const int64_t ubase = (int64_t)g * ucap;
+  uint32_t flags = 0;
+
+  int U = a.union_len[g];
+  if (U < 0 || U > ucap) {
+    flags |= SEL_ATTN_STATUS_UNION_LEN;
+    U = U < 0 ? 0 : (int)ucap;
+  }
+  // chunks of the union, rounded up to an even count so that the producers'
+  // two-iteration register rotation never exits half way (a trailing chunk
+  // past the union is all padding: chooser bytes and scales 0)
+  const int nch = (U + kChunk - 1) / kChunk;
+  const int nch_even = (nch + 1) & ~1;
+
+  if (wave < kConsumerWaves) {
+    consume(a, sm, g, h, nch_even, wave, lane);
+  } else {
+    const int ptid = tid - 64 * kConsumerWaves;
+    produce(a, sm, h, U, nch_even, ubase, ptid, wave == kConsumerWaves, flags);
   }
   if (flags) atomicOr(a.status, flags);
 }

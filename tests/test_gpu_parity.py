@@ -109,15 +109,13 @@ def test_attention_dense_workload_all_rows():
     _check_problem(synth.as_problem(synth.generate(w)), what=w.name)
 
 
-@pytest.mark.parametrize("idx,n_groups", [(1, 24), (2, 12), (3, 12), (4, 12)])
-def test_attention_workloads_sampled_groups(idx, n_groups):
-    """Full-size inputs in the benchmark's launch configuration; whole sampled groups."""
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_attention_workloads_all_rows(idx):
+    """Full-size inputs in the benchmark's launch configuration, every output."""
     w = synth.workload(idx)
     print("case", w.name, flush=True)
     d = synth.as_problem(synth.generate(w))
-    rows = H.sample_rows(w.n_q, n_groups, seed=idx)
-    out = _check_problem(d, rows=rows, what=w.name)
-    assert np.all(np.isfinite(out))
+    out = _check_problem(d, what=w.name)
     # a property that holds for every output: a convex combination of V rows
     vmax = float(np.abs(d["v_pool"].astype(np.float32) * d["v_scale"][..., None]).max())
     assert float(np.abs(out).max()) <= vmax * (1 + 1e-2)
