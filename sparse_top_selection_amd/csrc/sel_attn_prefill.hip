@@ -65,7 +65,7 @@ constexpr float kVFold = 1024.f;    // probabilities carry v_scale * 2^10 into F
 constexpr float kVScaleLimit = 4.f;
 
 struct __align__(16) Stage {
-  _Float16 k[kChunk * kD];     // [cell][dim], swizzled by k_unit()
+  _Float16 k[kChunk * kD];     // [cell][dim] holding k + 1152, swizzled by k_unit()
   _Float16 vt[kD * kChunk];    // [dim][slot], swizzled by v_unit()
   float kf[kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
   float vf[kChunk];            // v_scale * 2^10; 0 where unusable
@@ -73,9 +73,10 @@ struct __align__(16) Stage {
   uint32_t emask_spare[kChunk / 4];  // written by the producer wave that owns vf
 };
 
-struct Ring {
-  int32_t row[kChunk];         // pool row (phys * n_kv + h) * 64 + slot; -1 = unusable
-  uint8_t mask[kChunk];
+struct __align__(16) Ring {
+  uint32_t off[kChunk];        // byte offset of the cell's K/V row in a pool:
+                               // ((phys * n_kv + h) * 64 + slot) * 128; 0 = unusable
+  uint8_t mask[kChunk];        // chooser byte; 0 for unusable cells
 };
 
 struct __align__(16) Smem {
@@ -102,12 +103,13 @@ __device__ __forceinline__ half2 biased_pair_to_half2(uint32_t pair_bits) {
   return h - half2{(_Float16)1152.f, (_Float16)1152.f};
 }
 
-// four int8 in one dword -> four halves (bytes 0..3 in order)
-__device__ __forceinline__ half4 i8x4_to_half4(uint32_t w) {
+// four int8 in one dword -> the FP16 bit patterns of k + 1152 (exact), two per
+// dword. The K tile keeps this bias: the S^T accumulator starts at
+// -1152 * sum_d q_d instead of 0, which removes it (see consume()).
+__device__ __forceinline__ uint2 i8x4_to_biased_half(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;
-  const half2 lo = biased_pair_to_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
-  const half2 hi = biased_pair_to_half2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
-  return half4{lo.x, lo.y, hi.x, hi.y};
+  return uint2{__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u),
+               __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)};
 }
 
 // ---------------------------------------------------------------------------
@@ -143,23 +145,23 @@ __device__ __forceinline__ int v_unit_cell(int w, int k) {
 // 8*(t&15)..+7 (eight 8-byte loads, transposed to eight dims x eight cells).
 // Unusable cells (padding, non-resident, bad) read pool row 0, which always
 // exists; their chooser byte and scales are 0, so the values never count.
-__device__ __forceinline__ uint32_t row_bytes(int row) { return (uint32_t)max(row, 0) * kD; }
-
+// A scale is zeroed exactly when its cell's chooser byte is 0 (such a cell
+// contributes nothing either way).
 __device__ __forceinline__ u32x4 load_k_task(const PrefillArgs& a, const Ring& rg, int t) {
-  const uint32_t off = row_bytes(rg.row[t >> 3]) + 16u * (t & 7);
+  const uint32_t off = rg.off[t >> 3] + 16u * (t & 7);
   return *reinterpret_cast<const u32x4*>(a.k_pool + off);
 }
 
 __device__ __forceinline__ void store_k_task(Stage& st, int t, u32x4 raw) {
   const int cell = t >> 3;
   const int u0 = 2 * (t & 7);
-  const half4 h0 = i8x4_to_half4(raw.x), h1 = i8x4_to_half4(raw.y);
-  const half4 h2 = i8x4_to_half4(raw.z), h3 = i8x4_to_half4(raw.w);
-  const half8 a0 = half8{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-  const half8 a1 = half8{h2.x, h2.y, h2.z, h2.w, h3.x, h3.y, h3.z, h3.w};
+  const uint2 b0 = i8x4_to_biased_half(raw.x), b1 = i8x4_to_biased_half(raw.y);
+  const uint2 b2 = i8x4_to_biased_half(raw.z), b3 = i8x4_to_biased_half(raw.w);
+  const u32x4 a0 = u32x4{b0.x, b0.y, b1.x, b1.y};
+  const u32x4 a1 = u32x4{b2.x, b2.y, b3.x, b3.y};
   _Float16* base = st.k + cell * kD;
-  *reinterpret_cast<half8*>(base + (k_unit(u0, cell) << 3)) = a0;
-  *reinterpret_cast<half8*>(base + (k_unit(u0 + 1, cell) << 3)) = a1;
+  *reinterpret_cast<u32x4*>(base + (k_unit(u0, cell) << 3)) = a0;
+  *reinterpret_cast<u32x4*>(base + (k_unit(u0 + 1, cell) << 3)) = a1;
 }
 
 struct VRaw {
@@ -170,18 +172,17 @@ struct VRaw {
 __device__ __forceinline__ VRaw load_v_task(const PrefillArgs& a, const Ring& rg, int t) {
   const int w = t >> 4;
   const uint32_t d8 = 8u * (t & 15);
+  const u32x4 o0 = *reinterpret_cast<const u32x4*>(rg.off + v_unit_cell(w, 0));
+  const u32x4 o1 = *reinterpret_cast<const u32x4*>(rg.off + v_unit_cell(w, 1));
   VRaw r;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t off = row_bytes(rg.row[v_unit_cell(w, k >> 2) + (k & 3)]) + d8;
-    const uint2 x = *reinterpret_cast<const uint2*>(a.v_pool + off);
-    if (k < 4) {
-      r.lo0[k] = x.x;
-      r.hi0[k] = x.y;
-    } else {
-      r.lo1[k - 4] = x.x;
-      r.hi1[k - 4] = x.y;
-    }
+  for (int k = 0; k < 4; ++k) {
+    const uint2 x = *reinterpret_cast<const uint2*>(a.v_pool + o0[k] + d8);
+    const uint2 y = *reinterpret_cast<const uint2*>(a.v_pool + o1[k] + d8);
+    r.lo0[k] = x.x;
+    r.hi0[k] = x.y;
+    r.lo1[k] = y.x;
+    r.hi1[k] = y.y;
   }
   return r;
 }
@@ -266,18 +267,18 @@ __device__ __forceinline__ void finish_translation(const PrefillArgs& a, const P
   const bool page_bad = p.valid && !cell_bad && (p.page >= a.n_pages || p.page < -1);
   flags |= (cell_bad ? SEL_ATTN_STATUS_CELL_RANGE : 0u) | (page_bad ? SEL_ATTN_STATUS_PAGE_RANGE : 0u);
   const bool usable = p.valid && !cell_bad && !page_bad && p.page >= 0;
-  const int32_t row = usable ? (p.page * a.n_kv + h) * 64 + (p.cell & 63) : -1;
-  rg.row[lane] = row;
+  const uint32_t row = (uint32_t)((p.page * a.n_kv + h) * 64 + (p.cell & 63));
+  rg.off[lane] = usable ? row * kD : 0u;
   rg.mask[lane] = usable ? p.mask : (uint8_t)0;
 }
 
 // ---------------------------------------------------------------------------
 // Consumer waves 0..5: row block rb = w % 3 (32 rows), cell half ch = w / 3.
 __device__ __forceinline__ float16v scores_t(const Stage& st, const half8 qf[8], int ch, int hb,
-                                             int l32) {
+                                             int l32, float s_init) {
   float16v s;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  for (int r = 0; r < 16; ++r) s[r] = s_init;
   const int cell = 32 * ch + l32;
   const _Float16* krow = st.k + cell * kD;
 #pragma unroll
@@ -307,6 +308,7 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
                                         int nch_even, int wave, int lane) {
   const int rb = wave % 3;
   const int ch = wave / 3;
+  const bool late = wave == 4 || wave == 5;   // shares a SIMD with wave 0 / 1
   const int hb = lane >> 5;
   const int l32 = lane & 31;
   const int n_qh = a.n_kv * kQPerKv;
@@ -332,6 +334,15 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
     }
   }
 
+  // the K tile holds k + 1152: start every S^T accumulator at -1152 * sum_d q_d
+  // of this lane's row (its 64 dims here, the other 64 in lane ^ 32)
+  float qsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qsum += (float)qf[s][e];
+  const float s_init = -1152.f * (qsum + __shfl_xor(qsum, 32));
+
   lds_barrier();   // prologue: ring filled
   lds_barrier();   // prologue: chunks 0 and 1 staged, stage 3's V^T zeroed
 
@@ -350,7 +361,7 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   // the softmax of chunk c on the VALU while those MFMAs execute. The first
   // iteration multiplies a zeroed P^T with stage 3's V^T (zero-filled by the
   // producers); the last one computes a discarded S^T.
-  float16v s_cur = scores_t(sm.st[0], qf, ch, hb, l32);
+  float16v s_cur = scores_t(sm.st[0], qf, ch, hb, l32, s_init);
   half8 pb[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
@@ -360,30 +371,35 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   for (int c = 0; c < nch_even; ++c) {
     const Stage& st = sm.st[c % kStages];
     const Stage& st_prev = sm.st[(c + kStages - 1) % kStages];
+    const Stage& st_next = sm.st[(c + 1) % kStages];
 
-    // ---- matrix work that does not wait for this chunk's softmax
-    const float16v s_next = scores_t(sm.st[(c + 1) % kStages], qf, ch, hb, l32);
-    pv_accumulate(st_prev, pb, o, ch, hb, l32);
-
-    // ---- chooser masks (wave-uniform) and per-cell factors of chunk c
+    // ---- phase 1: LDS reads of chunk c's chooser bytes and factors and of
+    // chunk c-1's V^T operands
     const u32x4 em_lo = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch);
     const u32x4 em_hi = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch + 4);
+    float4v k4[4], v4[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+      v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
+    }
+    half8 frag[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ks = i >> 2, mb = i & 3;
+      const int d = 32 * mb + l32;
+      frag[i] = *reinterpret_cast<const half8*>(st_prev.vt + d * kChunk +
+                                                (v_unit(4 * ch + 2 * ks + hb, d) << 3));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 2: softmax of chunk c (VALU) interleaved with O^T += V^T P^T
+    // of chunk c-1 (MFMA)
     uint32_t em[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       em[k] = __builtin_amdgcn_readfirstlane(em_lo[k]);
       em[4 + k] = __builtin_amdgcn_readfirstlane(em_hi[k]);
-    }
-    float kf[16], vf[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4v k4 = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
-      const float4v v4 = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[4 * q4 + e] = k4[e];
-        vf[4 * q4 + e] = v4[e];
-      }
     }
     bool keep[16];
 #pragma unroll
@@ -393,34 +409,73 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
       const uint64_t lm = (uint64_t)(lo * 0x01010101u) | ((uint64_t)(hi * 0x01010101u) << 32);
       keep[r] = __builtin_amdgcn_inverse_ballot_w64(lm);
     }
-
-    // ---- masked online softmax of chunk c (log2 domain), P'^T into pb
-    float p[16];
     float psum = 0.f;
+    half8 pn[2];   // this chunk's P'^T (pb still feeds chunk c-1's MFMAs)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float u = keep[r] ? __builtin_fmaf(s_cur[r], kf[r], -m_run) : ninf;
-      p[r] = __builtin_amdgcn_exp2f(u);
-      psum += p[r];
+      const float u = keep[r] ? __builtin_fmaf(s_cur[r], k4[r >> 2][r & 3], -m_run) : ninf;
+      const float pr = __builtin_amdgcn_exp2f(u);
+      psum += pr;
+      pn[r >> 3][r & 7] = (_Float16)(pr * v4[r >> 2][r & 3]);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (_Float16)(p[r] * vf[r]);
+    for (int i = 0; i < 8; ++i)
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag[i], pb[i >> 2], o[i & 3], 0, 0, 0);
 
-    // interleave: one MFMA, then a few VALU / LDS-read instructions
+    // The second consumer wave of SIMDs 0 and 1 (waves 4, 5) takes the
+    // iteration's barrier here instead of at the end, so the two waves of a
+    // SIMD run their VALU-heavy and MFMA-heavy phases at different times.
+    // Every stage such a wave reads after this barrier (K of chunk c+1, and in
+    // the slow path chunk c's factors) is only rewritten two barriers later.
+    if (late) lds_barrier();
+
+    // ---- phase 3: chunk c+1's K operands (loaded as phase 2's MFMAs free
+    // their registers), its S^T chain interleaved with packing chunk c's P'^T
+    half8 kfrag[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int ks = 0; ks < 8; ++ks) {
+      const int cell = 32 * ch + l32;
+      kfrag[ks] = *reinterpret_cast<const half8*>(st_next.k + cell * kD +
+                                                  (k_unit(2 * ks + hb, cell) << 3));
+    }
+    float16v s_next;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_next[r] = s_init;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[ks], qf[ks], s_next, 0, 0, 0);
+    pb[0] = pn[0];
+    pb[1] = pn[1];
+    // schedule: PV MFMAs each followed by one K-operand load and a slice of
+    // the softmax, then the S^T chain
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);   // VALU incl. transcendental
-      __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);   // SALU
+      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);   // VALU incl. transcendental
+      __builtin_amdgcn_sched_group_barrier(0x004, 5, 0);   // SALU
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
+    // ---- phase 4: the lazy stabiliser check
     if (__ballot(!(psum <= kLazyLimit))) {
       // the running maximum moves: rescale what is accumulated (this waits
       // for the MFMAs issued above) and redo the chunk against the new maximum
+      // (its factors are read again from the stage, which is still intact)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+        v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
+      }
       float cmax = ninf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) cmax = fmaxf(cmax, keep[r] ? s_cur[r] * kf[r] : ninf);
+      for (int r = 0; r < 16; ++r)
+        cmax = fmaxf(cmax, keep[r] ? s_cur[r] * k4[r >> 2][r & 3] : ninf);
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
       const float m_new = fmaxf(m_run, cmax);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -433,16 +488,15 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
       psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float u = keep[r] ? __builtin_fmaf(s_cur[r], kf[r], -m_run) : ninf;
-        p[r] = __builtin_amdgcn_exp2f(u);
-        psum += p[r];
+        const float u = keep[r] ? __builtin_fmaf(s_cur[r], k4[r >> 2][r & 3], -m_run) : ninf;
+        const float pr = __builtin_amdgcn_exp2f(u);
+        psum += pr;
+        pb[r >> 3][r & 7] = (_Float16)(pr * v4[r >> 2][r & 3]);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (_Float16)(p[r] * vf[r]);
     }
     l_run += psum;
     s_cur = s_next;
-    lds_barrier();
+    if (!late) lds_barrier();
   }
   // the last chunk's P'^T
   if (nch_even > 0) pv_accumulate(sm.st[(nch_even - 1) % kStages], pb, o, ch, hb, l32);
@@ -507,10 +561,10 @@ __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int
 #pragma unroll
   for (int k = 0; k < 4; ++k) r.k[k] = load_k_task(a, rg, ptid + 128 * k);
   r.v = load_v_task(a, rg, ptid);
-  const int row = rg.row[ptid & 63];
+  const int cell = ptid & 63;
   const float* sp = (ptid < kChunk) ? a.k_scale : a.v_scale;
-  const float v = sp[max(row, 0)];
-  r.sc = row >= 0 ? v : 0.f;
+  const float v = sp[rg.off[cell] / kD];
+  r.sc = rg.mask[cell] ? v : 0.f;
 }
 
 __device__ __forceinline__ void convert(const PrefillArgs& a, Stage& st, const Ring& rg, int ptid,

@@ -134,13 +134,16 @@ def test_attention_random_selections_all_rows(seed, n_ctx, n_q, n_kv, dup, nonre
 
 
 def test_attention_exact_mean_catches_single_cell_errors():
-    """K = 0 and v_scale = 2^-6: every probability is exactly 1 in FP16, sums are
-    exact in FP32, so the output is 2^-6 * mean(v_int over the resident set) to
-    within 2 ulp. Dropping or adding one cell of ~2,000 would move it far more."""
+    """k_scale = 0 and v_scale = 2^-6: every logit is exactly 0, so every chosen
+    probability is exactly 1 in FP16 and the sums are exact in FP32; the output
+    is 2^-6 * mean(v_int over the resident set) to within 2 ulp. Dropping or
+    adding one cell of ~2,000 would move it far more. (Zero scales rather than
+    zero K integers: the kernel keeps K with a constant offset in its FP16 tile
+    and removes it in FP32, which is exact only up to rounding.)"""
     w = synth.workload(2)
     print("case exact mean", w.name, flush=True)
     d = synth.as_problem(synth.generate(w))
-    d["k_pool"] = np.zeros_like(d["k_pool"])
+    d["k_scale"] = np.zeros_like(d["k_scale"])
     d["v_scale"] = np.full_like(d["v_scale"], np.float32(2.0 ** -6))
     pt = d["page_table"].copy()
     pt[[3, 100, 257, 511]] = -1               # some pages not resident
