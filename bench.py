@@ -43,10 +43,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ctx32k_drift005")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
-                    help="query positions of the oracle's timed sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=-1,
+                    help="query positions of the oracle's timed sample (-1 = all of the chunk, 0 = skip)")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: no CPU leg, plus a 512 MiB copy for counter calibration")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="no GPU: turn the rocprofv3 output that profile.sh left in DIR into the "
+                         "summaries under profiles/")
     return ap.parse_args()
 
 
@@ -72,8 +75,85 @@ def counter_traffic(workload_name: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 512 << 20         # the calibration copy of --profile: bytes read, and bytes written
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0].split("<")[0].split("::")[-1]
+
+
+def summarize(d: str, workload: str):
+    """Summaries of a profile.sh run: the kernel-trace statistics as text, and the
+    HBM bytes per prefill launch from FETCH_SIZE / WRITE_SIZE, each counter scaled
+    by what it reads for a copy of COPY_BYTES (the copy kernel with the largest
+    grid in the run)."""
+    with open(os.path.join(d, "commands.txt")) as f:
+        commands = f.read().strip().splitlines()
+    stats = _csv_rows(os.path.join(d, "trace", "run_kernel_stats.csv"))
+    lines = ["rocprofv3 --kernel-trace --stats summary, workload %s" % workload,
+             "command: " + commands[0], "",
+             "%-28s %6s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "total_%")]
+    for r in stats:
+        lines.append("%-28s %6s %12.2f %12.2f %12.2f %12.2f" % (
+            _short(r["Name"])[:28], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "kernels_%s_stats.txt" % workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    rec = {"workload": workload, "source_hash": source_hash(), "commands": commands[1:3],
+           "copy_bytes": COPY_BYTES, "kernels": {}}
+    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = [r for r in _csv_rows(os.path.join(d, sub, "pmc_counter_collection.csv"))
+                if r["Counter_Name"] == counter]
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] or "copy" in _short(r["Kernel_Name"]).lower()]
+        big = max(int(r["Grid_Size"]) for r in copies)
+        copy_kib = np.mean([float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == big])
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        rec[counter] = {"copy_KiB": copy_kib, "factor": factor}
+        for k in ("sel_attn_prefill_kernel", "union_build_kernel"):
+            v = [float(r["Counter_Value"]) for r in rows if _short(r["Kernel_Name"]) == k]
+            ent = rec["kernels"].setdefault(k, {})
+            ent[counter + "_KiB_per_dispatch"] = float(np.mean(v))
+            ent[counter.split("_")[0].lower() + "_bytes"] = float(np.mean(v)) * 1024.0 * factor
+    for ent in rec["kernels"].values():
+        ent["hbm_bytes"] = ent["fetch_bytes"] + ent["write_bytes"]
+    rec["hbm_bytes_per_launch"] = rec["kernels"]["sel_attn_prefill_kernel"]["hbm_bytes"]
+    with open(os.path.join(ROOT, "profiles", "prefill_%s_counters.json" % workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines += ["", "HBM bytes per dispatch from counters (two --pmc runs, one counter each):"]
+    lines += ["command: " + c for c in commands[1:3]]
+    lines.append("calibration: a %d MiB device copy reads FETCH_SIZE %.0f KiB (factor %.4f) and "
+                 "WRITE_SIZE %.0f KiB (factor %.4f)" % (
+                     COPY_BYTES >> 20, rec["FETCH_SIZE"]["copy_KiB"], rec["FETCH_SIZE"]["factor"],
+                     rec["WRITE_SIZE"]["copy_KiB"], rec["WRITE_SIZE"]["factor"]))
+    for k, ent in rec["kernels"].items():
+        lines.append("%-28s FETCH %.0f KiB -> %.1f MB, WRITE %.0f KiB -> %.1f MB, total %.1f MB" % (
+            k, ent["FETCH_SIZE_KiB_per_dispatch"], ent["fetch_bytes"] / 1e6,
+            ent["WRITE_SIZE_KiB_per_dispatch"], ent["write_bytes"] / 1e6, ent["hbm_bytes"] / 1e6))
+    lines.append("kernel sources: sha256 prefix %s (the benchmark uses these bytes only while it "
+                 "matches)" % rec["source_hash"])
+    lines.append("made by: bash profile.sh OUTDIR; python3 bench.py --summarize OUTDIR")
+    with open(os.path.join(ROOT, "profiles", "kernels_%s_stats.txt" % workload), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(os.path.join(ROOT, "profiles", "kernels_%s_stats.txt" % workload)).read())
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.workload)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this path is measured on a single MI355X "
@@ -196,9 +276,9 @@ def main():
         "source_hash": source_hash(),
     }
 
-    if args.cpu_rows > 0 and not args.profile:
+    if args.cpu_rows != 0 and not args.profile:
         import oracle
-        n_rows = min(args.cpu_rows, w.n_q)
+        n_rows = w.n_q if args.cpu_rows < 0 else min(args.cpu_rows, w.n_q)
         rows = np.arange(n_rows, dtype=np.int32)
         cores = oracle.max_threads()
         c0 = time.perf_counter()
