@@ -58,21 +58,17 @@ constexpr int kChunk = 64;          // union cells per iteration
 constexpr int kD = 128;             // head dim
 constexpr int kQPerKv = 12;
 constexpr int kStages = 4;          // LDS tiles: chunks c-1 (V), c, c+1 (K), c+2 (being written)
-constexpr int kRing = 4;            // translated chunks c+2 .. c+4
+constexpr int kLead = 2;            // iterations between a read and its first use (producers)
+constexpr int kRing = 8;            // translated chunks (ring slots, indexed by chunk & 7)
 constexpr float kLazyLimit = 16.f;
 constexpr float kNoMax = -1e30f;    // stabiliser before a row has seen a chosen cell
 constexpr float kVFold = 1024.f;    // probabilities carry v_scale * 2^10 into FP16
 constexpr float kVScaleLimit = 4.f;
 
-struct __align__(16) Stage {
-  _Float16 k[kChunk * kD];     // [cell][dim] holding k + 1152, swizzled by k_unit()
-  _Float16 vt[kD * kChunk];    // [dim][slot], swizzled by v_unit()
-  float kf[kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
-  float vf[kChunk];            // v_scale * 2^10; 0 where unusable
-  uint32_t emask[kChunk / 4];  // chooser bytes, 0 for padding / non-resident cells
-  uint32_t emask_spare[kChunk / 4];  // written by the producer wave that owns vf
-};
-
+// LDS: the four stages' K tiles fill the first 64 KiB and their V^T tiles the
+// next 64 KiB, so that a stage's tile addresses differ by multiples of 16 KiB
+// that fit the 16-bit immediate offset of the LDS instructions (a per-lane
+// base register serves every stage).
 struct __align__(16) Ring {
   uint32_t off[kChunk];        // byte offset of the cell's K/V row in a pool:
                                // ((phys * n_kv + h) * 64 + slot) * 128; 0 = unusable
@@ -80,9 +76,28 @@ struct __align__(16) Ring {
 };
 
 struct __align__(16) Smem {
-  Stage st[kStages];
-  Ring ring[kRing + 1];   // the last slot takes the second producer wave's copy
+  _Float16 k[kStages][kChunk * kD];     // [cell][dim] holding k + 1152, swizzled by k_unit()
+  _Float16 vt[kStages][kD * kChunk];    // [dim][slot], swizzled by v_unit()
+  float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
+  float vf[kStages][kChunk];            // v_scale * 2^10; 0 where unusable
+  uint32_t emask[kStages][kChunk / 4];  // chooser bytes, 0 for padding / non-resident cells
+  uint32_t emask_spare[kStages][kChunk / 4];  // written by the producer wave that owns vf
+  Ring ring[kRing + 1];   // the last slot takes the second producer wave's copies
 };
+
+// One stage's parts.
+struct Stage {
+  _Float16* k;
+  _Float16* vt;
+  float* kf;
+  float* vf;
+  uint32_t* emask;
+  uint32_t* emask_spare;
+};
+
+__device__ __forceinline__ Stage stage(Smem& sm, int s) {
+  return Stage{sm.k[s], sm.vt[s], sm.kf[s], sm.vf[s], sm.emask[s], sm.emask_spare[s]};
+}
 
 // ---------------------------------------------------------------------------
 // Workgroup barrier that orders LDS only. Threads of a workgroup talk to each
@@ -152,7 +167,7 @@ __device__ __forceinline__ u32x4 load_k_task(const PrefillArgs& a, const Ring& r
   return *reinterpret_cast<const u32x4*>(a.k_pool + off);
 }
 
-__device__ __forceinline__ void store_k_task(Stage& st, int t, u32x4 raw) {
+__device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) {
   const int cell = t >> 3;
   const int u0 = 2 * (t & 7);
   const uint2 b0 = i8x4_to_biased_half(raw.x), b1 = i8x4_to_biased_half(raw.y);
@@ -207,7 +222,7 @@ __device__ __forceinline__ void transpose_quad(u32x4 raw, half4 out[4]) {
   }
 }
 
-__device__ __forceinline__ void store_v_task(Stage& st, int t, const VRaw& raw) {
+__device__ __forceinline__ void store_v_task(const Stage& st, int t, const VRaw& raw) {
   const int w = t >> 4;
   const int d0 = 8 * (t & 15);
   half4 a0[4], a1[4], b0[4], b1[4];
@@ -227,49 +242,61 @@ __device__ __forceinline__ void store_v_task(Stage& st, int t, const VRaw& raw) 
 }
 
 // ---------------------------------------------------------------------------
-// Page translation of one chunk cell (producer wave 6, one lane per cell), in
-// three steps spread over two iterations so that no global read sits on the
-// critical path: read the union entry, then the page-table entry, then form
-// the pool row.
-struct Pending {
+// Page translation of one chunk cell (one lane per cell), in three steps whose
+// global reads are each consumed kLead iterations after they were issued (the
+// same lead as the K/V gathers, so that no wait for an early read also waits
+// for gathers still in flight): read the union entry, then the page-table
+// entry, then form the pool row and publish it in the ring.
+// Records carry only loaded words (each in a register of its own: packing a
+// field next to another would read the in-flight load at once); whether an
+// entry lies inside the union is recomputed from the chunk index.
+struct UnionRec {
   int32_t cell;
-  uint8_t mask;
-  int32_t page;    // page-table entry, once read
-  bool valid;
+  uint32_t mask;
 };
 
-// All three steps are branch-free (clamped, always-valid addresses plus selects)
-// so that a producer iteration stays one basic block and the compiler's memory
-// waits can let a chunk's loads run across the barrier into the next iteration.
-__device__ __forceinline__ Pending read_union_entry(const PrefillArgs& a, int64_t ubase, int U,
-                                                    int cc, int lane) {
+struct PageRec {
+  int32_t cell;
+  uint32_t mask;
+  int32_t page_raw;   // page_table entry (of page 0 when the cell is not in [0, n_ctx))
+};
+
+__device__ __forceinline__ bool in_union(int U, int cc, int lane) { return cc * kChunk + lane < U; }
+
+// All steps are branch-free (clamped, always-valid addresses plus selects) so
+// that a producer iteration stays one basic block.
+__device__ __forceinline__ UnionRec read_union_entry(const PrefillArgs& a, int64_t ubase, int U,
+                                                     int cc, int lane) {
   // union rows hold at least 8 entries, so index 0 is always readable
-  const int idx = cc * kChunk + lane;
-  const bool valid = idx < U;
-  const int64_t at = ubase + (valid ? idx : 0);
-  Pending p;
-  p.cell = a.union_cells[at];
-  p.mask = a.union_mask[at];
-  p.page = -1;
-  p.valid = valid;
+  const int64_t at = ubase + (in_union(U, cc, lane) ? cc * kChunk + lane : 0);
+  UnionRec u;
+  u.cell = a.union_cells[at];
+  u.mask = a.union_mask[at];
+  return u;
+}
+
+__device__ __forceinline__ PageRec read_page_entry(const PrefillArgs& a, const UnionRec& u) {
+  PageRec p;
+  p.cell = u.cell;
+  p.mask = u.mask;
+  const bool in_ctx = u.cell >= 0 && u.cell < a.n_ctx;
+  p.page_raw = a.page_table[in_ctx ? (u.cell >> 6) : 0];
   return p;
 }
 
-__device__ __forceinline__ void read_page_entry(const PrefillArgs& a, Pending& p) {
-  const bool in_ctx = p.valid && p.cell >= 0 && p.cell < a.n_ctx;
-  const int32_t e = a.page_table[in_ctx ? (p.cell >> 6) : 0];
-  p.page = in_ctx ? e : -1;
-}
-
-__device__ __forceinline__ void finish_translation(const PrefillArgs& a, const Pending& p, int h,
-                                                   Ring& rg, int lane, uint32_t& flags) {
-  const bool cell_bad = p.valid && (p.cell < 0 || p.cell >= a.n_ctx);
-  const bool page_bad = p.valid && !cell_bad && (p.page >= a.n_pages || p.page < -1);
+__device__ __forceinline__ void finish_translation(const PrefillArgs& a, const PageRec& p, int U,
+                                                   int cc, int h, Ring& rg, int lane,
+                                                   uint32_t& flags) {
+  const bool valid = in_union(U, cc, lane);
+  const bool in_ctx = valid && p.cell >= 0 && p.cell < a.n_ctx;
+  const int32_t page = in_ctx ? p.page_raw : -1;
+  const bool cell_bad = valid && !in_ctx;
+  const bool page_bad = in_ctx && (page >= a.n_pages || page < -1);
   flags |= (cell_bad ? SEL_ATTN_STATUS_CELL_RANGE : 0u) | (page_bad ? SEL_ATTN_STATUS_PAGE_RANGE : 0u);
-  const bool usable = p.valid && !cell_bad && !page_bad && p.page >= 0;
-  const uint32_t row = (uint32_t)((p.page * a.n_kv + h) * 64 + (p.cell & 63));
+  const bool usable = in_ctx && !page_bad && page >= 0;
+  const uint32_t row = (uint32_t)((page * a.n_kv + h) * 64 + (p.cell & 63));
   rg.off[lane] = usable ? row * kD : 0u;
-  rg.mask[lane] = usable ? p.mask : (uint8_t)0;
+  rg.mask[lane] = (uint8_t)(usable ? p.mask : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,10 +332,9 @@ __device__ __forceinline__ void pv_accumulate(const Stage& st, const half8 pb[2]
 }
 
 __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
-                                        int nch_even, int wave, int lane) {
+                                        int nch, int wave, int lane) {
   const int rb = wave % 3;
   const int ch = wave / 3;
-  const bool late = wave == 4 || wave == 5;   // shares a SIMD with wave 0 / 1
   const int hb = lane >> 5;
   const int l32 = lane & 31;
   const int n_qh = a.n_kv * kQPerKv;
@@ -361,17 +387,17 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   // the softmax of chunk c on the VALU while those MFMAs execute. The first
   // iteration multiplies a zeroed P^T with stage 3's V^T (zero-filled by the
   // producers); the last one computes a discarded S^T.
-  float16v s_cur = scores_t(sm.st[0], qf, ch, hb, l32, s_init);
+  float16v s_cur = scores_t(stage(sm, 0), qf, ch, hb, l32, s_init);
   half8 pb[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb[ks][e] = (_Float16)0.f;
 
-  for (int c = 0; c < nch_even; ++c) {
-    const Stage& st = sm.st[c % kStages];
-    const Stage& st_prev = sm.st[(c + kStages - 1) % kStages];
-    const Stage& st_next = sm.st[(c + 1) % kStages];
+  for (int c = 0; c < nch; ++c) {
+    const Stage st = stage(sm, c % kStages);
+    const Stage st_prev = stage(sm, (c + kStages - 1) % kStages);
+    const Stage st_next = stage(sm, (c + 1) % kStages);
 
     // ---- phase 1: LDS reads of chunk c's chooser bytes and factors and of
     // chunk c-1's V^T operands
@@ -421,13 +447,6 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag[i], pb[i >> 2], o[i & 3], 0, 0, 0);
-
-    // The second consumer wave of SIMDs 0 and 1 (waves 4, 5) takes the
-    // iteration's barrier here instead of at the end, so the two waves of a
-    // SIMD run their VALU-heavy and MFMA-heavy phases at different times.
-    // Every stage such a wave reads after this barrier (K of chunk c+1, and in
-    // the slow path chunk c's factors) is only rewritten two barriers later.
-    if (late) lds_barrier();
 
     // ---- phase 3: chunk c+1's K operands (loaded as phase 2's MFMAs free
     // their registers), its S^T chain interleaved with packing chunk c's P'^T
@@ -496,14 +515,14 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
     }
     l_run += psum;
     s_cur = s_next;
-    if (!late) lds_barrier();
+    lds_barrier();
   }
   // the last chunk's P'^T
-  if (nch_even > 0) pv_accumulate(sm.st[(nch_even - 1) % kStages], pb, o, ch, hb, l32);
+  if (nch > 0) pv_accumulate(stage(sm, (nch - 1) % kStages), pb, o, ch, hb, l32);
   lds_barrier();   // every wave is done with the tiles the merge reuses
 
   // ---- merge the two cell halves of each row block and write the output
-  float* xo = reinterpret_cast<float*>(&sm.st[0]);   // [3][16 float4 groups][64 lanes][4]
+  float* xo = reinterpret_cast<float*>(&sm.k[0][0]);   // [3][16 float4 groups][64 lanes][4]
   float* xm = xo + 3 * 64 * 64;                      // [3][64]
   float* xl = xm + 3 * 64;                           // [3][64]
   if (ch == 1) {
@@ -554,7 +573,8 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 struct Raw {
   u32x4 k[4];
   VRaw v;
-  float sc;
+  float sc;     // k scale (wave 6) or v scale (wave 7) of cell ptid & 63 (row 0's if unusable)
+  uint32_t m;   // chooser byte of that cell; 0 if unusable
 };
 
 __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int ptid, Raw& r) {
@@ -563,12 +583,12 @@ __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int
   r.v = load_v_task(a, rg, ptid);
   const int cell = ptid & 63;
   const float* sp = (ptid < kChunk) ? a.k_scale : a.v_scale;
-  const float v = sp[rg.off[cell] / kD];
-  r.sc = rg.mask[cell] ? v : 0.f;
+  r.sc = sp[rg.off[cell] / kD];   // zeroed at conversion, when the load has landed
+  r.m = rg.mask[cell];
 }
 
-__device__ __forceinline__ void convert(const PrefillArgs& a, Stage& st, const Ring& rg, int ptid,
-                                        const Raw& r, uint32_t& flags) {
+__device__ __forceinline__ void convert(const PrefillArgs& a, const Stage& st, int ptid, const Raw& r,
+                                        uint32_t& flags) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) store_k_task(st, ptid + 128 * k, r.k[k]);
   store_v_task(st, ptid, r.v);
@@ -576,73 +596,105 @@ __device__ __forceinline__ void convert(const PrefillArgs& a, Stage& st, const R
   // a spare copy of the chooser bytes), without a branch
   const bool kwave = ptid < kChunk;
   const int lane = ptid & 63;
-  const bool v_ok = fabsf(r.sc) < kVScaleLimit;
+  const float sc = r.m ? r.sc : 0.f;
+  const bool v_ok = fabsf(sc) < kVScaleLimit;
   flags |= (!kwave && !v_ok) ? SEL_ATTN_STATUS_V_SCALE : 0u;
-  const float f = kwave ? r.sc * a.score_scale : (v_ok ? r.sc * kVFold : 0.f);
-  (kwave ? st.kf : st.vf)[lane] = f;
-  reinterpret_cast<uint8_t*>(kwave ? st.emask : st.emask_spare)[lane] = rg.mask[lane];
+  const float mult = kwave ? a.score_scale : (v_ok ? kVFold : 0.f);
+  (kwave ? st.kf : st.vf)[lane] = sc * mult;
+  reinterpret_cast<uint8_t*>(kwave ? st.emask : st.emask_spare)[lane] = (uint8_t)r.m;
 }
 
-__device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, int U,
-                                        int nch_even, int64_t ubase, int ptid, bool translator,
-                                        uint32_t& flags) {
-  // prologue: chunks 0..3 translated, page entry of chunk 4 read, union entry
-  // of chunk 5 read; chunks 0 and 1 staged, chunk 2 gathered. Both producer
-  // waves translate the same lanes; wave 7 writes its copy to the spare slot.
+// Producer state, each array indexed by chunk & 3: gathered rows (chunk x is
+// gathered in iteration x-2-kLead and converted in x-2), union records (read in
+// x-4-3*kLead, consumed in x-4-2*kLead) and page records (read then, consumed
+// in x-4-kLead, when the ring slot of chunk x is written). Every index below is
+// a compile-time constant once a step is instantiated for its phase P = c & 3,
+// so the sets stay in registers and the stage addresses fold into immediates.
+constexpr int kAheadGather = 2 + kLead;        // chunk gathered in iteration c: c + 5
+constexpr int kAheadFinish = 3 + kLead;        // ring slot written: c + 6
+constexpr int kAheadPage = 3 + 2 * kLead;      // page entry read: c + 9
+constexpr int kAheadUnion = 3 + 3 * kLead;     // union entry read: c + 12
+
+struct ProdState {
+  Raw raw[4];
+  UnionRec un[4];
+  PageRec pg[4];
+};
+
+// Iteration c (phase P = c & 3), while the consumers work on chunks c-1..c+1.
+// Reads are issued union, page, gather (oldest consumer first), and each one
+// issued here is consumed kLead iterations later.
+template <int P>
+__device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, ProdState& ps, int c,
+                                             int h, int U, int64_t ubase, int ptid, bool translator,
+                                             uint32_t& flags) {
   const int lane = ptid & 63;
-  auto ring_slot = [&](int cc) -> Ring& { return sm.ring[translator ? (cc % kRing) : kRing]; };
-  // Translation state alternates between two register sets so that every
-  // global read is consumed exactly one iteration after it was issued (no
-  // register copies of in-flight loads): a_* = union entry read, page entry
-  // next; b_* = page entry read, pool row next.
-  Pending a0, a1, b0, b1;
+  ps.un[(P + kAheadUnion) & 3] = read_union_entry(a, ubase, U, c + kAheadUnion, lane);
+  ps.pg[(P + kAheadPage) & 3] = read_page_entry(a, ps.un[(P + kAheadPage) & 3]);
+  const int cf = c + kAheadFinish;
+  finish_translation(a, ps.pg[(P + kAheadFinish) & 3], U, cf, h,
+                     sm.ring[translator ? (cf & (kRing - 1)) : kRing], lane, flags);
+  gather(a, sm.ring[(c + kAheadGather) & (kRing - 1)], ptid, ps.raw[(P + kAheadGather) & 3]);
+  convert(a, stage(sm, (P + 2) & 3), ptid, ps.raw[(P + 2) & 3], flags);
+  lds_barrier();
+}
+
+__device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, int U, int nch,
+                                        int64_t ubase, int ptid, bool translator,
+                                        uint32_t& flags) {
+  static_assert(kLead >= 1 && kLead <= 3 && kStages == 4 && kAheadFinish <= kRing,
+                "register sets and ring slots cover the lead");
+  const int lane = ptid & 63;
+  ProdState ps;
+  // prologue: what iteration 0 expects. Chunks below kAheadFinish translated
+  // into their ring slots; page records of the next kLead chunks and union
+  // records of the kLead after those read; chunks 0 and 1 staged, chunks 2 ..
+  // kAheadGather-1 gathered. Both producer waves translate the same lanes;
+  // wave 7 writes its copy to the spare slot.
   {
-    Pending p[kRing];
+    UnionRec u[kAheadPage];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) p[i] = read_union_entry(a, ubase, U, i, lane);
-    b1 = read_union_entry(a, ubase, U, kRing, lane);
-    a1 = read_union_entry(a, ubase, U, kRing + 1, lane);
+    for (int i = 0; i < kAheadPage; ++i) u[i] = read_union_entry(a, ubase, U, i, lane);
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) read_page_entry(a, p[i]);
-    read_page_entry(a, b1);
+    for (int i = kAheadPage; i < kAheadUnion; ++i) ps.un[i & 3] = read_union_entry(a, ubase, U, i, lane);
+    PageRec p[kAheadFinish];
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) finish_translation(a, p[i], h, ring_slot(i), lane, flags);
+    for (int i = 0; i < kAheadFinish; ++i) p[i] = read_page_entry(a, u[i]);
+#pragma unroll
+    for (int i = kAheadFinish; i < kAheadPage; ++i) ps.pg[i & 3] = read_page_entry(a, u[i]);
+#pragma unroll
+    for (int i = 0; i < kAheadFinish; ++i)
+      finish_translation(a, p[i], U, i, h, sm.ring[translator ? i : kRing], lane, flags);
   }
   // stage 3's V^T meets a zeroed P^T in the consumers' first iteration: keep
   // it finite
   {
-    u32x4* z = reinterpret_cast<u32x4*>(sm.st[kStages - 1].vt);
+    u32x4* z = reinterpret_cast<u32x4*>(sm.vt[kStages - 1]);
 #pragma unroll
     for (int i = 0; i < (kD * kChunk * 2) / (16 * 128); ++i) z[ptid + 128 * i] = u32x4{0u, 0u, 0u, 0u};
   }
   lds_barrier();
-  Raw set0, set1;
-  gather(a, sm.ring[0], ptid, set0);
-  gather(a, sm.ring[1], ptid, set1);
-  convert(a, sm.st[0], sm.ring[0], ptid, set0, flags);
-  gather(a, sm.ring[2], ptid, set0);
-  convert(a, sm.st[1], sm.ring[1], ptid, set1, flags);
+#pragma unroll
+  for (int x = 0; x < kAheadGather; ++x) {
+    if (x >= 4) convert(a, stage(sm, x - 4), ptid, ps.raw[x & 3], flags);   // frees the set
+    gather(a, sm.ring[x], ptid, ps.raw[x & 3]);
+  }
+#pragma unroll
+  for (int x = (kAheadGather > 4 ? kAheadGather - 4 : 0); x < 2; ++x)
+    convert(a, stage(sm, x), ptid, ps.raw[x & 3], flags);
   lds_barrier();
 
-  // Iteration c: gather chunk c+3 into one register set, finish the
-  // translation of chunk c+4, read the page entry of chunk c+5 and the union
-  // entry of chunk c+6, convert chunk c+2 from the other set. Chunks past the
-  // end are harmless: their ring rows are -1 (row 0 is read, masks and scales
-  // are 0) and their stages are never read for results.
-  auto step = [&](int c, Raw& load_set, Raw& conv_set, Pending& a_in, Pending& a_out,
-                  Pending& b_in, Pending& b_out) {
-    gather(a, sm.ring[(c + 3) % kRing], ptid, load_set);
-    finish_translation(a, b_in, h, ring_slot(c + 4), lane, flags);   // chunk c+4
-    b_out = a_in;
-    read_page_entry(a, b_out);                                         // chunk c+5
-    a_out = read_union_entry(a, ubase, U, c + 6, lane);                // chunk c+6
-    convert(a, sm.st[(c + 2) % kStages], sm.ring[(c + 2) % kRing], ptid, conv_set, flags);
-    lds_barrier();
-  };
-  for (int c = 0; c < nch_even; c += 2) {
-    step(c, set1, set0, a1, a0, b1, b0);
-    step(c + 1, set0, set1, a0, a1, b0, b1);
+  int c = 0;
+  for (; c + 4 <= nch; c += 4) {
+    produce_step<0>(a, sm, ps, c, h, U, ubase, ptid, translator, flags);
+    produce_step<1>(a, sm, ps, c + 1, h, U, ubase, ptid, translator, flags);
+    produce_step<2>(a, sm, ps, c + 2, h, U, ubase, ptid, translator, flags);
+    produce_step<3>(a, sm, ps, c + 3, h, U, ubase, ptid, translator, flags);
   }
+  const int rem = nch - c;   // 0..3 more iterations, phases 0, 1, 2
+  if (rem > 0) produce_step<0>(a, sm, ps, c, h, U, ubase, ptid, translator, flags);
+  if (rem > 1) produce_step<1>(a, sm, ps, c + 1, h, U, ubase, ptid, translator, flags);
+  if (rem > 2) produce_step<2>(a, sm, ps, c + 2, h, U, ubase, ptid, translator, flags);
   lds_barrier();   // consumers finish their last O^T update
   lds_barrier();   // merge of the consumers' two cell halves
 }
@@ -668,17 +720,13 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
     flags |= SEL_ATTN_STATUS_UNION_LEN;
     U = U < 0 ? 0 : (int)ucap;
   }
-  // chunks of the union, rounded up to an even count so that the producers'
-  // two-iteration register rotation never exits half way (a trailing chunk
-  // past the union is all padding: chooser bytes and scales 0)
-  const int nch = (U + kChunk - 1) / kChunk;
-  const int nch_even = (nch + 1) & ~1;
+  const int nch = (U + kChunk - 1) / kChunk;   // 64-cell chunks of the union
 
   if (wave < kConsumerWaves) {
-    consume(a, sm, g, h, nch_even, wave, lane);
+    consume(a, sm, g, h, nch, wave, lane);
   } else {
     const int ptid = tid - 64 * kConsumerWaves;
-    produce(a, sm, h, U, nch_even, ubase, ptid, wave == kConsumerWaves, flags);
+    produce(a, sm, h, U, nch, ubase, ptid, wave == kConsumerWaves, flags);
   }
   if (flags) atomicOr(a.status, flags);
 }
