@@ -58,17 +58,17 @@ constexpr int kChunk = 64;          // union cells per iteration
 constexpr int kD = 128;             // head dim
 constexpr int kQPerKv = 12;
 constexpr int kStages = 4;          // LDS tiles: chunks c-1 (V), c, c+1 (K), c+2 (being written)
-constexpr int kLead = 2;            // iterations between a read and its first use (producers)
+constexpr int kKRow = kD + 8;       // K tile row: 128 dims + 16 bytes of padding
+constexpr int kLead = 3;            // iterations between a read and its first use (producers)
 constexpr int kRing = 8;            // translated chunks (ring slots, indexed by chunk & 7)
 constexpr float kLazyLimit = 16.f;
 constexpr float kNoMax = -1e30f;    // stabiliser before a row has seen a chosen cell
 constexpr float kVFold = 1024.f;    // probabilities carry v_scale * 2^10 into FP16
 constexpr float kVScaleLimit = 4.f;
 
-// LDS: the four stages' K tiles fill the first 64 KiB and their V^T tiles the
-// next 64 KiB, so that a stage's tile addresses differ by multiples of 16 KiB
-// that fit the 16-bit immediate offset of the LDS instructions (a per-lane
-// base register serves every stage).
+// LDS: the four stages' K tiles, then their V tiles, so that a stage's tile
+// addresses differ by multiples of the tile size that fit the 16-bit immediate
+// offset of the LDS instructions (a per-lane base register serves every stage).
 struct __align__(16) Ring {
   uint32_t off[kChunk];        // byte offset of the cell's K/V row in a pool:
                                // ((phys * n_kv + h) * 64 + slot) * 128; 0 = unusable
@@ -76,8 +76,8 @@ struct __align__(16) Ring {
 };
 
 struct __align__(16) Smem {
-  _Float16 k[kStages][kChunk * kD];     // [cell][dim] holding k + 1152, swizzled by k_unit()
-  _Float16 vt[kStages][kD * kChunk];    // [dim][slot], swizzled by v_unit()
+  _Float16 k[kStages][kChunk * kKRow];  // [cell][dim] holding k + 1152, rows of kKRow
+  _Float16 v[kStages][kChunk * kD];     // [cell][dim], swizzled by v_pos()
   float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
   float vf[kStages][kChunk];            // v_scale * 2^10; 0 where unusable
   uint32_t emask[kStages][kChunk / 4];  // chooser bytes, 0 for padding / non-resident cells
@@ -88,7 +88,7 @@ struct __align__(16) Smem {
 // One stage's parts.
 struct Stage {
   _Float16* k;
-  _Float16* vt;
+  _Float16* v;
   float* kf;
   float* vf;
   uint32_t* emask;
@@ -96,7 +96,7 @@ struct Stage {
 };
 
 __device__ __forceinline__ Stage stage(Smem& sm, int s) {
-  return Stage{sm.k[s], sm.vt[s], sm.kf[s], sm.vf[s], sm.emask[s], sm.emask_spare[s]};
+  return Stage{sm.k[s], sm.v[s], sm.kf[s], sm.vf[s], sm.emask[s], sm.emask_spare[s]};
 }
 
 // ---------------------------------------------------------------------------
@@ -133,38 +133,30 @@ __device__ __forceinline__ uint2 i8x4_to_biased_half(uint32_t w) {
 // conflicts (8 consecutive lanes always touch 8 distinct units of a 128-byte
 // bank period).
 //
-// K tile [cell][dim], 16 units of 8 dims per cell row. Unit u (dims 8u..8u+7)
-// of cell c lives at rot(u) ^ (c & 15), rot(u) = ((u & 1) << 3) | (u >> 1).
-// Consumers load unit 2ks+hb of 8 consecutive cells; producers store units 2p
-// and 2p+1 (p = 0..7) of one cell.
-__device__ __forceinline__ int k_unit(int u, int cell) {
-  return (((u & 1) << 3) | (u >> 1)) ^ (cell & 15);
-}
-
-// V^T tile [dim][slot], 8 units of 8 cells per dim row. Unit w = 4ch + 2ks + hb
-// holds cells 16(2ch+ks) + 4hb + {0..3} then the same + 8: the order in which a
-// lane of the S^T accumulator holds its cells, so P^T feeds the PV MFMA from
-// registers. Unit w of dim d lives at w ^ vswz(d), vswz(d) = (d ^ (d >> 3)) & 7.
-// Consumers load unit w of 8 consecutive dims; producers store unit w of dims
-// 8k + jd for 8 consecutive k.
-__device__ __forceinline__ int v_unit(int w, int d) { return w ^ ((d ^ (d >> 3)) & 7); }
-
-// first cell of the k-th 4-cell quad (k = 0, 1) held by V^T unit w
-__device__ __forceinline__ int v_unit_cell(int w, int k) {
-  return 16 * (w >> 1) + 4 * (w & 1) + 8 * k;
+// K tile [cell][dim], rows of 272 bytes (128 dims + 16 bytes of padding): the
+// 16 consecutive cells a consumer half-wave reads at one 16-byte unit fall on
+// 16 distinct bank groups, and so do the two cells x eight even (or odd) units
+// that 16 producer lanes store; every consumer K address is one base plus an
+// immediate.
+// V tile [cell][dim], rows of 256 bytes, unit u of cell c at u ^ vswz(c),
+// vswz(c) = ((c & 3) << 2) | (c & 1). Producers store units 2p and 2p+1 of one
+// cell per 8 lanes (16 lanes: two cells of opposite parity, even and odd
+// positions); consumers read it transposed, 8 bytes per lane, four
+// consecutive cells x 64 bytes per 32 lanes (4(mb ^ x) + (v ^ (x & 1)) are 16
+// distinct positions). Both are free of bank conflicts.
+__device__ __forceinline__ int v_pos(int u, int cell) {
+  return u ^ (((cell & 3) << 2) | (cell & 1));
 }
 
 // ---------------------------------------------------------------------------
-// Producer staging tasks. K task t in [0,512): cell t>>3, dims 16*(t&7)..+15 (one
-// 16-byte load). V task t in [0,128): unit w = t>>4 (eight cells), dims
-// 8*(t&15)..+7 (eight 8-byte loads, transposed to eight dims x eight cells).
+// Producer staging tasks. Task t in [0,512): cell t>>3, dims 16*(t&7)..+15, one
+// 16-byte load from the K pool and one from the V pool at the same offset.
 // Unusable cells (padding, non-resident, bad) read pool row 0, which always
 // exists; their chooser byte and scales are 0, so the values never count.
 // A scale is zeroed exactly when its cell's chooser byte is 0 (such a cell
 // contributes nothing either way).
-__device__ __forceinline__ u32x4 load_k_task(const PrefillArgs& a, const Ring& rg, int t) {
-  const uint32_t off = rg.off[t >> 3] + 16u * (t & 7);
-  return *reinterpret_cast<const u32x4*>(a.k_pool + off);
+__device__ __forceinline__ uint32_t task_offset(const Ring& rg, int t) {
+  return rg.off[t >> 3] + 16u * (t & 7);
 }
 
 __device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) {
@@ -174,71 +166,25 @@ __device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) 
   const uint2 b2 = i8x4_to_biased_half(raw.z), b3 = i8x4_to_biased_half(raw.w);
   const u32x4 a0 = u32x4{b0.x, b0.y, b1.x, b1.y};
   const u32x4 a1 = u32x4{b2.x, b2.y, b3.x, b3.y};
-  _Float16* base = st.k + cell * kD;
-  *reinterpret_cast<u32x4*>(base + (k_unit(u0, cell) << 3)) = a0;
-  *reinterpret_cast<u32x4*>(base + (k_unit(u0 + 1, cell) << 3)) = a1;
+  _Float16* base = st.k + cell * kKRow + 8 * u0;
+  *reinterpret_cast<u32x4*>(base) = a0;
+  *reinterpret_cast<u32x4*>(base + 8) = a1;
 }
 
-struct VRaw {
-  u32x4 lo0, lo1;   // dims 8dq..8dq+3 of the unit's first / second cell quad
-  u32x4 hi0, hi1;   // dims 8dq+4..8dq+7
-};
-
-__device__ __forceinline__ VRaw load_v_task(const PrefillArgs& a, const Ring& rg, int t) {
-  const int w = t >> 4;
-  const uint32_t d8 = 8u * (t & 15);
-  const u32x4 o0 = *reinterpret_cast<const u32x4*>(rg.off + v_unit_cell(w, 0));
-  const u32x4 o1 = *reinterpret_cast<const u32x4*>(rg.off + v_unit_cell(w, 1));
-  VRaw r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint2 x = *reinterpret_cast<const uint2*>(a.v_pool + o0[k] + d8);
-    const uint2 y = *reinterpret_cast<const uint2*>(a.v_pool + o1[k] + d8);
-    r.lo0[k] = x.x;
-    r.hi0[k] = x.y;
-    r.lo1[k] = y.x;
-    r.hi1[k] = y.y;
-  }
-  return r;
+__device__ __forceinline__ half8 unbias(uint2 lo, uint2 hi) {
+  const half2 a = biased_pair_to_half2(lo.x), b = biased_pair_to_half2(lo.y);
+  const half2 c = biased_pair_to_half2(hi.x), d = biased_pair_to_half2(hi.y);
+  return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-// four int8 dwords (cells 0..3, bytes = dims 0..3) -> for each dim jd the four
-// cells' halves, via a 4x4 byte transpose and the biased FP16 trick.
-__device__ __forceinline__ void transpose_quad(u32x4 raw, half4 out[4]) {
-  const uint32_t w0 = raw.x ^ 0x80808080u, w1 = raw.y ^ 0x80808080u;
-  const uint32_t w2 = raw.z ^ 0x80808080u, w3 = raw.w ^ 0x80808080u;
-  const uint32_t t01lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // c0d0 c1d0 c0d1 c1d1
-  const uint32_t t01hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // c0d2 c1d2 c0d3 c1d3
-  const uint32_t t23lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
-  const uint32_t t23hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
-  const uint32_t src01[2] = {t01lo, t01hi};
-  const uint32_t src23[2] = {t23lo, t23hi};
-#pragma unroll
-  for (int jd = 0; jd < 4; ++jd) {
-    const uint32_t sel = (jd & 1) ? 0x04030402u : 0x04010400u;
-    const half2 a01 = biased_pair_to_half2(__builtin_amdgcn_perm(0x64646464u, src01[jd >> 1], sel));
-    const half2 a23 = biased_pair_to_half2(__builtin_amdgcn_perm(0x64646464u, src23[jd >> 1], sel));
-    out[jd] = half4{a01.x, a01.y, a23.x, a23.y};
-  }
-}
-
-__device__ __forceinline__ void store_v_task(const Stage& st, int t, const VRaw& raw) {
-  const int w = t >> 4;
-  const int d0 = 8 * (t & 15);
-  half4 a0[4], a1[4], b0[4], b1[4];
-  transpose_quad(raw.lo0, a0);
-  transpose_quad(raw.lo1, a1);
-  transpose_quad(raw.hi0, b0);
-  transpose_quad(raw.hi1, b1);
-#pragma unroll
-  for (int jd = 0; jd < 4; ++jd) {
-    const int d = d0 + jd;
-    *reinterpret_cast<half8*>(st.vt + d * kChunk + (v_unit(w, d) << 3)) =
-        half8{a0[jd].x, a0[jd].y, a0[jd].z, a0[jd].w, a1[jd].x, a1[jd].y, a1[jd].z, a1[jd].w};
-    const int e = d0 + 4 + jd;
-    *reinterpret_cast<half8*>(st.vt + e * kChunk + (v_unit(w, e) << 3)) =
-        half8{b0[jd].x, b0[jd].y, b0[jd].z, b0[jd].w, b1[jd].x, b1[jd].y, b1[jd].z, b1[jd].w};
-  }
+__device__ __forceinline__ void store_v_task(const Stage& st, int t, u32x4 raw) {
+  const int cell = t >> 3;
+  const int u0 = 2 * (t & 7);
+  const half8 a0 = unbias(i8x4_to_biased_half(raw.x), i8x4_to_biased_half(raw.y));
+  const half8 a1 = unbias(i8x4_to_biased_half(raw.z), i8x4_to_biased_half(raw.w));
+  _Float16* base = st.v + cell * kD;
+  *reinterpret_cast<half8*>(base + (v_pos(u0, cell) << 3)) = a0;
+  *reinterpret_cast<half8*>(base + (v_pos(u0 + 1, cell) << 3)) = a1;
 }
 
 // ---------------------------------------------------------------------------
@@ -307,28 +253,165 @@ __device__ __forceinline__ float16v scores_t(const Stage& st, const half8 qf[8],
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = s_init;
   const int cell = 32 * ch + l32;
-  const _Float16* krow = st.k + cell * kD;
+  const _Float16* krow = st.k + cell * kKRow + 8 * hb;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const half8 ka = *reinterpret_cast<const half8*>(krow + (k_unit(2 * ks + hb, cell) << 3));
+    const half8 ka = *reinterpret_cast<const half8*>(krow + 16 * ks);
     s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], s, 0, 0, 0);
   }
   return s;
 }
 
-// O^T (128 dims x 32 rows) += V^T (dims x this wave's 32 cells) P'^T
-__device__ __forceinline__ void pv_accumulate(const Stage& st, const half8 pb[2], float16v o[4],
-                                              int ch, int hb, int l32) {
+// The A operand of O^T (dims 32mb + 0..31) += V^T P'^T for k-step ks, read
+// transposed from the [cell][dim] V tile with ds_read_b64_tr_b16: within each
+// group of 16 lanes, lane i receives element i % 4 of the 8-byte rows addressed
+// by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4. Lane l addresses cell
+// 32ch + 16ks + 4hb + ((l & 15) >> 2) (and the same + 8 for the second half)
+// at dims 32mb + 16((l >> 4) & 1) + 4(l & 3), so it receives dim 32mb + (l & 31)
+// of the eight cells whose P'^T values it holds, in the same order.
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+__device__ __forceinline__ half8 load_v_operand(const Stage& st, int ch, int ks, int mb, int lane) {
+  const int hb = lane >> 5;
+  const int c0 = 32 * ch + 16 * ks + 4 * hb + ((lane & 15) >> 2);
+  const int dimb = 64 * mb + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // byte in the row
+  const int pos = v_pos(dimb >> 4, c0);   // the same for cell c0 + 8
+  const char* row0 = reinterpret_cast<const char*>(st.v) + c0 * (kD * 2) + (pos << 4) + (dimb & 15);
+  typedef __attribute__((address_space(3))) fp16x4_t* lds_ptr;
+  const fp16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_ptr)(row0));
+  const fp16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_ptr)(row0 + 8 * kD * 2));
+  return half8{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3],
+               (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
+}
+
+// Registers a consumer wave carries from one iteration to the next.
+struct ConsState {
+  float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^10
+  float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
+  half8 pb[2];        // P'^T of the previous chunk
+  half8 vfrag[8];     // V^T operands of the previous chunk
+  float m_run;        // running maximum (log2 domain) of this lane's row
+  float l_run;        // running sum of probabilities against m_run
+};
+
+// Iteration c (phase P = c & 3; stage P holds chunk c). On entry S^T(c) is
+// complete and P'^T(c-1) with chunk c-1's V^T operands is in registers. The
+// iteration issues O^T += V^T P'^T for chunk c-1 first (its operands need no
+// wait, and it covers the latency of this iteration's LDS reads), then the
+// S^T(c+1) chain with the softmax of chunk c placed between its MFMAs, two
+// scores per MFMA, so the matrix pipe and the VALU work at the same time.
+template <int P>
+__device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half8 qf[8],
+                                             float s_init, int ch, int hb, int l32) {
+  const Stage st = stage(sm, P);
+  const Stage st_next = stage(sm, (P + 1) & 3);
+  const float ninf = -__builtin_inff();
+
+  // LDS reads: chunk c's chooser bytes and k factors
+  const u32x4 em_lo = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch);
+  const u32x4 em_hi = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch + 4);
+  float4v k4[4], v4[4];
+  k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
+  k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
+
+  // O^T += V^T P'^T of chunk c-1, then the first two of chunk c+1's K operands
+  // (the others are read two MFMAs ahead of their use in the chain below)
+  half8 kfrag[8];
+  const int cell = 32 * ch + l32;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int j = 0; j < 8; ++j)
+    cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[j], cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int d = 32 * mb + l32;
-      const int w = 4 * ch + 2 * ks + hb;
-      const half8 va = *reinterpret_cast<const half8*>(st.vt + d * kChunk + (v_unit(w, d) << 3));
-      o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[ks], o[mb], 0, 0, 0);
+  for (int j = 0; j < 2; ++j)
+    kfrag[j] = *reinterpret_cast<const half8*>(st_next.k + cell * kKRow + 8 * hb + 16 * j);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // per-score lane masks: the chooser byte replicated over the 8 rows of each
+  // position group (row n's bit is n & 7 = lane & 7)
+  uint32_t em[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    em[k] = __builtin_amdgcn_readfirstlane(em_lo[k]);
+    em[4 + k] = __builtin_amdgcn_readfirstlane(em_hi[k]);
+  }
+  bool keep[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t lo = (em[2 * (r >> 2)] >> (8 * (r & 3))) & 0xffu;
+    const uint32_t hi = (em[2 * (r >> 2) + 1] >> (8 * (r & 3))) & 0xffu;
+    const uint64_t lm = (uint64_t)(lo * 0x01010101u) | ((uint64_t)(hi * 0x01010101u) << 32);
+    keep[r] = __builtin_amdgcn_inverse_ballot_w64(lm);
+  }
+
+  // S^T(c+1) chain, the softmax of chunk c between its MFMAs
+  float16v s_next;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s_next[r] = s_init;
+  float pr[16];
+  float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qf[j], s_next, 0, 0, 0);
+    if (j + 2 < 8)
+      kfrag[j + 2] = *reinterpret_cast<const half8*>(st_next.k + cell * kKRow + 8 * hb + 16 * (j + 2));
+#pragma unroll
+    for (int r = 2 * j; r < 2 * j + 2; ++r) {
+      const float u = keep[r] ? __builtin_fmaf(cs.s_cur[r], k4[r >> 2][r & 3], -cs.m_run) : ninf;
+      pr[r] = __builtin_amdgcn_exp2f(u);
+    }
+    psum0 += pr[2 * j];
+    psum1 += pr[2 * j + 1];
+    if (j == 1 || j == 3) {   // k factors two MFMAs ahead of their scores
+      const int q4 = (j + 3) >> 1;
+      k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+    }
+    if (j == 5) {   // v factors, into registers the first K operands held
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float psum = psum0 + psum1;
+
+  // the lazy stabiliser: only when some lane's chunk sum leaves (0, 16] is the
+  // running maximum moved (what is accumulated is rescaled; this waits for the
+  // MFMAs issued above) and the chunk redone against it
+  if (__ballot(!(psum <= kLazyLimit))) {
+    float cmax = ninf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      cmax = fmaxf(cmax, keep[r] ? cs.s_cur[r] * k4[r >> 2][r & 3] : ninf);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(cs.m_run, cmax);
+    const float alpha = __builtin_amdgcn_exp2f(cs.m_run - m_new);
+    cs.m_run = m_new;
+    cs.l_run *= alpha;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs.o[mb][r] *= alpha;
+    psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float u = keep[r] ? __builtin_fmaf(cs.s_cur[r], k4[r >> 2][r & 3], -cs.m_run) : ninf;
+      pr[r] = __builtin_amdgcn_exp2f(u);
+      psum += pr[r];
     }
   }
+  cs.l_run += psum;
+
+  // P'^T of chunk c (probabilities times v_scale * 2^10, in FP16), the B
+  // operand of the next iteration's O^T update
+#pragma unroll
+  for (int r = 0; r < 16; ++r) cs.pb[r >> 3][r & 7] = (_Float16)(pr[r] * v4[r >> 2][r & 3]);
+
+  // chunk c's V^T operands for the next iteration (stage P is rewritten two
+  // barriers from now)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cs.vfrag[i] = load_v_operand(st, ch, i >> 2, i & 3, (hb << 5) | l32);
+  cs.s_cur = s_next;
+  lds_barrier();
 }
 
 __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
@@ -370,155 +453,44 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   const float s_init = -1152.f * (qsum + __shfl_xor(qsum, 32));
 
   lds_barrier();   // prologue: ring filled
-  lds_barrier();   // prologue: chunks 0 and 1 staged, stage 3's V^T zeroed
+  lds_barrier();   // prologue: chunks 0 and 1 staged
 
-  // running softmax state of this lane's row (over this wave's cell half)
-  float m_run = kNoMax;
-  float l_run = 0.f;
-  float16v o[4];
+  ConsState cs;
+  cs.m_run = kNoMax;
+  cs.l_run = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
-  const float ninf = -__builtin_inff();
-
-  // Software pipeline: iteration c issues the MFMAs of S^T(c+1) and of
-  // O^T += V^T P^T for chunk c-1 (whose P^T is already in registers), then runs
-  // the softmax of chunk c on the VALU while those MFMAs execute. The first
-  // iteration multiplies a zeroed P^T with stage 3's V^T (zero-filled by the
-  // producers); the last one computes a discarded S^T.
-  float16v s_cur = scores_t(stage(sm, 0), qf, ch, hb, l32, s_init);
-  half8 pb[2];
+    for (int r = 0; r < 16; ++r) cs.o[mb][r] = 0.f;
+  // the first iteration's O^T update multiplies zero operands
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs.vfrag[i][e] = (_Float16)0.f;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pb[ks][e] = (_Float16)0.f;
+    for (int e = 0; e < 8; ++e) cs.pb[ks][e] = (_Float16)0.f;
+  cs.s_cur = scores_t(stage(sm, 0), qf, ch, hb, l32, s_init);
 
-  for (int c = 0; c < nch; ++c) {
-    const Stage st = stage(sm, c % kStages);
-    const Stage st_prev = stage(sm, (c + kStages - 1) % kStages);
-    const Stage st_next = stage(sm, (c + 1) % kStages);
-
-    // ---- phase 1: LDS reads of chunk c's chooser bytes and factors and of
-    // chunk c-1's V^T operands
-    const u32x4 em_lo = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch);
-    const u32x4 em_hi = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch + 4);
-    float4v k4[4], v4[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
-      v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
-    }
-    half8 frag[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ks = i >> 2, mb = i & 3;
-      const int d = 32 * mb + l32;
-      frag[i] = *reinterpret_cast<const half8*>(st_prev.vt + d * kChunk +
-                                                (v_unit(4 * ch + 2 * ks + hb, d) << 3));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- phase 2: softmax of chunk c (VALU) interleaved with O^T += V^T P^T
-    // of chunk c-1 (MFMA)
-    uint32_t em[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      em[k] = __builtin_amdgcn_readfirstlane(em_lo[k]);
-      em[4 + k] = __builtin_amdgcn_readfirstlane(em_hi[k]);
-    }
-    bool keep[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t lo = (em[2 * (r >> 2)] >> (8 * (r & 3))) & 0xffu;
-      const uint32_t hi = (em[2 * (r >> 2) + 1] >> (8 * (r & 3))) & 0xffu;
-      const uint64_t lm = (uint64_t)(lo * 0x01010101u) | ((uint64_t)(hi * 0x01010101u) << 32);
-      keep[r] = __builtin_amdgcn_inverse_ballot_w64(lm);
-    }
-    float psum = 0.f;
-    half8 pn[2];   // this chunk's P'^T (pb still feeds chunk c-1's MFMAs)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float u = keep[r] ? __builtin_fmaf(s_cur[r], k4[r >> 2][r & 3], -m_run) : ninf;
-      const float pr = __builtin_amdgcn_exp2f(u);
-      psum += pr;
-      pn[r >> 3][r & 7] = (_Float16)(pr * v4[r >> 2][r & 3]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag[i], pb[i >> 2], o[i & 3], 0, 0, 0);
-
-    // ---- phase 3: chunk c+1's K operands (loaded as phase 2's MFMAs free
-    // their registers), its S^T chain interleaved with packing chunk c's P'^T
-    half8 kfrag[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int cell = 32 * ch + l32;
-      kfrag[ks] = *reinterpret_cast<const half8*>(st_next.k + cell * kD +
-                                                  (k_unit(2 * ks + hb, cell) << 3));
-    }
-    float16v s_next;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s_next[r] = s_init;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[ks], qf[ks], s_next, 0, 0, 0);
-    pb[0] = pn[0];
-    pb[1] = pn[1];
-    // schedule: PV MFMAs each followed by one K-operand load and a slice of
-    // the softmax, then the S^T chain
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);   // VALU incl. transcendental
-      __builtin_amdgcn_sched_group_barrier(0x004, 5, 0);   // SALU
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- phase 4: the lazy stabiliser check
-    if (__ballot(!(psum <= kLazyLimit))) {
-      // the running maximum moves: rescale what is accumulated (this waits
-      // for the MFMAs issued above) and redo the chunk against the new maximum
-      // (its factors are read again from the stage, which is still intact)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
-        v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
-      }
-      float cmax = ninf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        cmax = fmaxf(cmax, keep[r] ? s_cur[r] * k4[r >> 2][r & 3] : ninf);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-      psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float u = keep[r] ? __builtin_fmaf(s_cur[r], k4[r >> 2][r & 3], -m_run) : ninf;
-        const float pr = __builtin_amdgcn_exp2f(u);
-        psum += pr;
-        pb[r >> 3][r & 7] = (_Float16)(pr * v4[r >> 2][r & 3]);
-      }
-    }
-    l_run += psum;
-    s_cur = s_next;
-    lds_barrier();
+  int c = 0;
+  for (; c + 4 <= nch; c += 4) {
+    consume_step<0>(cs, sm, qf, s_init, ch, hb, l32);
+    consume_step<1>(cs, sm, qf, s_init, ch, hb, l32);
+    consume_step<2>(cs, sm, qf, s_init, ch, hb, l32);
+    consume_step<3>(cs, sm, qf, s_init, ch, hb, l32);
   }
-  // the last chunk's P'^T
-  if (nch > 0) pv_accumulate(stage(sm, (nch - 1) % kStages), pb, o, ch, hb, l32);
+  const int rem = nch - c;
+  if (rem > 0) consume_step<0>(cs, sm, qf, s_init, ch, hb, l32);
+  if (rem > 1) consume_step<1>(cs, sm, qf, s_init, ch, hb, l32);
+  if (rem > 2) consume_step<2>(cs, sm, qf, s_init, ch, hb, l32);
+  // the last chunk's O^T update (its V^T operands were loaded by the last step)
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    cs.o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[i], cs.pb[i >> 2], cs.o[i & 3], 0, 0, 0);
+  const float m_run = cs.m_run;
+  const float l_run = cs.l_run;
+  float16v* o = cs.o;
   lds_barrier();   // every wave is done with the tiles the merge reuses
 
   // ---- merge the two cell halves of each row block and write the output
@@ -568,19 +540,22 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 // consumers work on chunks c and c+1): translate chunk c+4 (union entry read two
 // iterations earlier, page entry one), gather chunk c+3 into registers, convert
 // chunk c+2 (gathered one iteration earlier) into its LDS stage. Each thread
-// owns K tasks ptid + 128k (k = 0..3) and V task ptid, and
-// the k scale (ptid < 64) or v scale of cell ptid & 63; wave 6 translates.
+// owns tasks ptid + 128k (k = 0..3) of both pools, and the k scale (ptid < 64)
+// or v scale of cell ptid & 63; wave 6 translates.
 struct Raw {
   u32x4 k[4];
-  VRaw v;
+  u32x4 v[4];
   float sc;     // k scale (wave 6) or v scale (wave 7) of cell ptid & 63 (row 0's if unusable)
   uint32_t m;   // chooser byte of that cell; 0 if unusable
 };
 
 __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int ptid, Raw& r) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) r.k[k] = load_k_task(a, rg, ptid + 128 * k);
-  r.v = load_v_task(a, rg, ptid);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t off = task_offset(rg, ptid + 128 * k);
+    r.k[k] = *reinterpret_cast<const u32x4*>(a.k_pool + off);
+    r.v[k] = *reinterpret_cast<const u32x4*>(a.v_pool + off);
+  }
   const int cell = ptid & 63;
   const float* sp = (ptid < kChunk) ? a.k_scale : a.v_scale;
   r.sc = sp[rg.off[cell] / kD];   // zeroed at conversion, when the load has landed
@@ -590,8 +565,10 @@ __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int
 __device__ __forceinline__ void convert(const PrefillArgs& a, const Stage& st, int ptid, const Raw& r,
                                         uint32_t& flags) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) store_k_task(st, ptid + 128 * k, r.k[k]);
-  store_v_task(st, ptid, r.v);
+  for (int k = 0; k < 4; ++k) {
+    store_k_task(st, ptid + 128 * k, r.k[k]);
+    store_v_task(st, ptid + 128 * k, r.v[k]);
+  }
   // wave 6 stores the k factors and chooser bytes, wave 7 the v factors (and
   // a spare copy of the chooser bytes), without a branch
   const bool kwave = ptid < kChunk;
@@ -666,13 +643,6 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
     for (int i = 0; i < kAheadFinish; ++i)
       finish_translation(a, p[i], U, i, h, sm.ring[translator ? i : kRing], lane, flags);
   }
-  // stage 3's V^T meets a zeroed P^T in the consumers' first iteration: keep
-  // it finite
-  {
-    u32x4* z = reinterpret_cast<u32x4*>(sm.vt[kStages - 1]);
-#pragma unroll
-    for (int i = 0; i < (kD * kChunk * 2) / (16 * 128); ++i) z[ptid + 128 * i] = u32x4{0u, 0u, 0u, 0u};
-  }
   lds_barrier();
 #pragma unroll
   for (int x = 0; x < kAheadGather; ++x) {
@@ -725,6 +695,9 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
   if (wave < kConsumerWaves) {
     consume(a, sm, g, h, nch, wave, lane);
   } else {
+    // the producers' work paces every wave (all wait for its stage at the
+    // barrier), so their instructions go first on the SIMDs they share
+    __builtin_amdgcn_s_setprio(1);
     const int ptid = tid - 64 * kConsumerWaves;
     produce(a, sm, h, U, nch, ubase, ptid, wave == kConsumerWaves, flags);
   }
