@@ -111,13 +111,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// INT8 -> FP16: bias each byte to unsigned (v + 128), place it under the FP16
-// exponent of 1024 (bit pattern 0x64XX = 1024 + XX), subtract 1152 exactly.
-__device__ __forceinline__ half2 biased_pair_to_half2(uint32_t pair_bits) {
-  half2 h = __builtin_bit_cast(half2, pair_bits);
-  return h - half2{(_Float16)1152.f, (_Float16)1152.f};
-}
-
+// INT8 -> FP16: bias each byte to unsigned (v + 128) and place it under the
+// FP16 exponent of 1024 (bit pattern 0x64XX = 1024 + XX): the exact FP16 value
+// of v + 1152.
 // four int8 in one dword -> the FP16 bit patterns of k + 1152 (exact), two per
 // dword. The K tile keeps this bias: the S^T accumulator starts at
 // -1152 * sum_d q_d instead of 0, which removes it (see consume()).
@@ -171,20 +167,16 @@ __device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) 
   *reinterpret_cast<u32x4*>(base + 8) = a1;
 }
 
-__device__ __forceinline__ half8 unbias(uint2 lo, uint2 hi) {
-  const half2 a = biased_pair_to_half2(lo.x), b = biased_pair_to_half2(lo.y);
-  const half2 c = biased_pair_to_half2(hi.x), d = biased_pair_to_half2(hi.y);
-  return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-
+// The V tile keeps v + 1152 too: the consumers track the sum of the FP16
+// probabilities they multiply with it and remove 1152 times that sum at the end.
 __device__ __forceinline__ void store_v_task(const Stage& st, int t, u32x4 raw) {
   const int cell = t >> 3;
   const int u0 = 2 * (t & 7);
-  const half8 a0 = unbias(i8x4_to_biased_half(raw.x), i8x4_to_biased_half(raw.y));
-  const half8 a1 = unbias(i8x4_to_biased_half(raw.z), i8x4_to_biased_half(raw.w));
+  const uint2 b0 = i8x4_to_biased_half(raw.x), b1 = i8x4_to_biased_half(raw.y);
+  const uint2 b2 = i8x4_to_biased_half(raw.z), b3 = i8x4_to_biased_half(raw.w);
   _Float16* base = st.v + cell * kD;
-  *reinterpret_cast<half8*>(base + (v_pos(u0, cell) << 3)) = a0;
-  *reinterpret_cast<half8*>(base + (v_pos(u0 + 1, cell) << 3)) = a1;
+  *reinterpret_cast<u32x4*>(base + (v_pos(u0, cell) << 3)) = u32x4{b0.x, b0.y, b1.x, b1.y};
+  *reinterpret_cast<u32x4*>(base + (v_pos(u0 + 1, cell) << 3)) = u32x4{b2.x, b2.y, b3.x, b3.y};
 }
 
 // ---------------------------------------------------------------------------
@@ -288,19 +280,23 @@ __device__ __forceinline__ half8 load_v_operand(const Stage& st, int ch, int ks,
 struct ConsState {
   float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^10
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
-  half8 pb[2];        // P'^T of the previous chunk
-  half8 vfrag[8];     // V^T operands of the previous chunk
+  half8 pb[2];        // P'^T of the previous chunk (of this chunk in kPvLast steps)
   float m_run;        // running maximum (log2 domain) of this lane's row
   float l_run;        // running sum of probabilities against m_run
+  float lp;           // running sum of this lane's FP16 P'^T values (the V tile
+                      // holds v + 1152: O^T carries 1152 times the row's sum)
 };
 
 // Iteration c (phase P = c & 3; stage P holds chunk c). On entry S^T(c) is
-// complete and P'^T(c-1) with chunk c-1's V^T operands is in registers. The
-// iteration issues O^T += V^T P'^T for chunk c-1 first (its operands need no
-// wait, and it covers the latency of this iteration's LDS reads), then the
-// S^T(c+1) chain with the softmax of chunk c placed between its MFMAs, two
-// scores per MFMA, so the matrix pipe and the VALU work at the same time.
-template <int P>
+// complete. The iteration runs the S^T(c+1) chain with the softmax of chunk c
+// placed between its MFMAs, two scores per MFMA, so the matrix pipe and the
+// VALU work at the same time, and one O^T += V^T P'^T update:
+//   kPvLast = false: chunk c-1's, issued first (its P'^T and V^T operands are
+//     in registers, and it covers the latency of the iteration's LDS reads);
+//   kPvLast = true: chunk c's, issued last, after its P'^T is formed.
+// The two waves that share a SIMD use the two orders, so that one issues its
+// O^T update while the other runs its softmax.
+template <int P, bool kPvLast>
 __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half8 qf[8],
                                              float s_init, int ch, int hb, int l32) {
   const Stage st = stage(sm, P);
@@ -318,9 +314,14 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half
   // (the others are read two MFMAs ahead of their use in the chain below)
   half8 kfrag[8];
   const int cell = 32 * ch + l32;
+  if (!kPvLast) {
+    const Stage st_prev = stage(sm, (P + 3) & 3);
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[j], cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      const half8 va = load_v_operand(st_prev, ch, j >> 2, j & 3, (hb << 5) | l32);
+      cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     kfrag[j] = *reinterpret_cast<const half8*>(st_next.k + cell * kKRow + 8 * hb + 16 * j);
@@ -387,6 +388,7 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half
     const float alpha = __builtin_amdgcn_exp2f(cs.m_run - m_new);
     cs.m_run = m_new;
     cs.l_run *= alpha;
+    cs.lp *= alpha;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -405,13 +407,42 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half
   // operand of the next iteration's O^T update
 #pragma unroll
   for (int r = 0; r < 16; ++r) cs.pb[r >> 3][r & 7] = (_Float16)(pr[r] * v4[r >> 2][r & 3]);
-
-  // chunk c's V^T operands for the next iteration (stage P is rewritten two
-  // barriers from now)
+  {
+    const half2 one = {(_Float16)1.f, (_Float16)1.f};
+    float lp = cs.lp;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cs.vfrag[i] = load_v_operand(st, ch, i >> 2, i & 3, (hb << 5) | l32);
+    for (int k = 0; k < 8; ++k) {
+      const half2 pair = {cs.pb[k >> 2][2 * (k & 3)], cs.pb[k >> 2][2 * (k & 3) + 1]};
+      lp = __builtin_amdgcn_fdot2(pair, one, lp, false);
+    }
+    cs.lp = lp;
+  }
+
+  if (kPvLast) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const half8 va = load_v_operand(st, ch, j >> 2, j & 3, (hb << 5) | l32);
+      cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
+    }
+  }
   cs.s_cur = s_next;
   lds_barrier();
+}
+
+template <bool kPvLast>
+__device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, const half8 qf[8],
+                                               float s_init, int ch, int hb, int l32, int nch) {
+  int c = 0;
+  for (; c + 4 <= nch; c += 4) {
+    consume_step<0, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+    consume_step<1, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+    consume_step<2, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+    consume_step<3, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+  }
+  const int rem = nch - c;
+  if (rem > 0) consume_step<0, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+  if (rem > 1) consume_step<1, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+  if (rem > 2) consume_step<2, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
 }
 
 __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
@@ -458,36 +489,41 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   ConsState cs;
   cs.m_run = kNoMax;
   cs.l_run = 0.f;
+  cs.lp = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) cs.o[mb][r] = 0.f;
-  // the first iteration's O^T update multiplies zero operands
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cs.vfrag[i][e] = (_Float16)0.f;
+  // a zero P'^T (with stage 3's V tile zeroed by the producers) for the first
+  // iteration's update of the previous chunk
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) cs.pb[ks][e] = (_Float16)0.f;
   cs.s_cur = scores_t(stage(sm, 0), qf, ch, hb, l32, s_init);
 
-  int c = 0;
-  for (; c + 4 <= nch; c += 4) {
-    consume_step<0>(cs, sm, qf, s_init, ch, hb, l32);
-    consume_step<1>(cs, sm, qf, s_init, ch, hb, l32);
-    consume_step<2>(cs, sm, qf, s_init, ch, hb, l32);
-    consume_step<3>(cs, sm, qf, s_init, ch, hb, l32);
-  }
-  const int rem = nch - c;
-  if (rem > 0) consume_step<0>(cs, sm, qf, s_init, ch, hb, l32);
-  if (rem > 1) consume_step<1>(cs, sm, qf, s_init, ch, hb, l32);
-  if (rem > 2) consume_step<2>(cs, sm, qf, s_init, ch, hb, l32);
-  // the last chunk's O^T update (its V^T operands were loaded by the last step)
+  if (wave < 4) {
+    consume_chunks<false>(cs, sm, qf, s_init, ch, hb, l32, nch);
+    // the last chunk's O^T update
+    if (nch > 0) {
+      const Stage st_last = stage(sm, (nch - 1) & 3);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    cs.o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[i], cs.pb[i >> 2], cs.o[i & 3], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) {
+        const half8 va = load_v_operand(st_last, ch, j >> 2, j & 3, (hb << 5) | l32);
+        cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
+      }
+    }
+  } else {
+    consume_chunks<true>(cs, sm, qf, s_init, ch, hb, l32, nch);
+  }
+  // remove the V tile's offset: 1152 times the row's sum of P'^T values
+  {
+    const float corr = 1152.f * (cs.lp + __shfl_xor(cs.lp, 32));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs.o[mb][r] -= corr;
+  }
   const float m_run = cs.m_run;
   const float l_run = cs.l_run;
   float16v* o = cs.o;
@@ -642,6 +678,13 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
 #pragma unroll
     for (int i = 0; i < kAheadFinish; ++i)
       finish_translation(a, p[i], U, i, h, sm.ring[translator ? i : kRing], lane, flags);
+  }
+  // stage 3's V tile meets the zero P'^T of the consumers' first update: keep
+  // it finite
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(sm.v[kStages - 1]);
+#pragma unroll
+    for (int i = 0; i < (kD * kChunk * 2) / (16 * 128); ++i) z[ptid + 128 * i] = u32x4{0u, 0u, 0u, 0u};
   }
   lds_barrier();
 #pragma unroll
