@@ -57,8 +57,10 @@ constexpr int kThreads = 64 * (kConsumerWaves + kProducerWaves);
 constexpr int kChunk = 64;          // union cells per iteration
 constexpr int kD = 128;             // head dim
 constexpr int kQPerKv = 12;
-constexpr int kStages = 4;          // LDS tiles: chunks c-1 (V), c, c+1 (K), c+2 (being written)
-constexpr int kKRow = kD + 8;       // K tile row: 128 dims + 16 bytes of padding
+constexpr int kStages = 4;          // V tiles and factors: chunks c (read), c+1, c+2 (written)
+constexpr int kKStages = 2;         // K tiles: chunks c+1 (read), c+2 (written)
+constexpr int kRows = 8 * kQPerKv;  // rows of a work-group: 8 positions x 12 query heads
+constexpr int kKRow = kD + 8;       // K and Q tile rows: 128 dims + 16 bytes of padding
 constexpr int kLead = 3;            // iterations between a read and its first use (producers)
 constexpr int kRing = 8;            // translated chunks (ring slots, indexed by chunk & 7)
 constexpr float kLazyLimit = 16.f;
@@ -76,16 +78,17 @@ struct __align__(16) Ring {
 };
 
 struct __align__(16) Smem {
-  _Float16 k[kStages][kChunk * kKRow];  // [cell][dim] holding k + 1152, rows of kKRow
+  _Float16 k[kKStages][kChunk * kKRow]; // [cell][dim] holding k + 1152, rows of kKRow
   _Float16 v[kStages][kChunk * kD];     // [cell][dim], swizzled by v_pos()
   float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
   float vf[kStages][kChunk];            // v_scale * 2^10; 0 where unusable
   uint32_t emask[kStages][kChunk / 4];  // chooser bytes, 0 for padding / non-resident cells
   uint32_t emask_spare[kStages][kChunk / 4];  // written by the producer wave that owns vf
+  _Float16 q[kRows * kKRow];            // the work-group's Q, [row][dim] in FP16, rows of kKRow
   Ring ring[kRing + 1];   // the last slot takes the second producer wave's copies
 };
 
-// One stage's parts.
+// The parts of the stages that hold chunk c.
 struct Stage {
   _Float16* k;
   _Float16* v;
@@ -95,8 +98,9 @@ struct Stage {
   uint32_t* emask_spare;
 };
 
-__device__ __forceinline__ Stage stage(Smem& sm, int s) {
-  return Stage{sm.k[s], sm.v[s], sm.kf[s], sm.vf[s], sm.emask[s], sm.emask_spare[s]};
+__device__ __forceinline__ Stage stage(Smem& sm, int c) {
+  const int s = c & (kStages - 1);
+  return Stage{sm.k[c & (kKStages - 1)], sm.v[s], sm.kf[s], sm.vf[s], sm.emask[s], sm.emask_spare[s]};
 }
 
 // ---------------------------------------------------------------------------
@@ -239,7 +243,9 @@ __device__ __forceinline__ void finish_translation(const PrefillArgs& a, const P
 
 // ---------------------------------------------------------------------------
 // Consumer waves 0..5: row block rb = w % 3 (32 rows), cell half ch = w / 3.
-__device__ __forceinline__ float16v scores_t(const Stage& st, const half8 qf[8], int ch, int hb,
+// S^T (this wave's 32 cells x 32 rows) of one chunk. qrow: this lane's row of
+// the Q tile, at dims 8hb (k-step ks reads dims 16ks + 8hb .. +7).
+__device__ __forceinline__ float16v scores_t(const Stage& st, const _Float16* qrow, int ch, int hb,
                                              int l32, float s_init) {
   float16v s;
 #pragma unroll
@@ -249,7 +255,8 @@ __device__ __forceinline__ float16v scores_t(const Stage& st, const half8 qf[8],
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const half8 ka = *reinterpret_cast<const half8*>(krow + 16 * ks);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[ks], s, 0, 0, 0);
+    const half8 qb = *reinterpret_cast<const half8*>(qrow + 16 * ks);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb, s, 0, 0, 0);
   }
   return s;
 }
@@ -276,72 +283,73 @@ __device__ __forceinline__ half8 load_v_operand(const Stage& st, int ch, int ks,
                (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
 }
 
+// Lane mask of the lanes whose byte E of w is nonzero: one VALU compare with a
+// byte-select operand (the compiler would spend an AND and a compare).
+template <int E>
+__device__ __forceinline__ uint64_t byte_nonzero(uint32_t w) {
+  uint64_t m;
+  asm("v_cmp_ne_u32_sdwa %0, %1, %2 src0_sel:BYTE_%3 src1_sel:DWORD"
+      : "=s"(m)
+      : "v"(w), "v"(0u), "n"(E));
+  return m;
+}
+
 // Registers a consumer wave carries from one iteration to the next.
 struct ConsState {
   float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^10
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
-  half8 pb[2];        // P'^T of the previous chunk (of this chunk in kPvLast steps)
+  half8 pb[2];        // P'^T of the current chunk, once formed
   float m_run;        // running maximum (log2 domain) of this lane's row
   float l_run;        // running sum of probabilities against m_run
   float lp;           // running sum of this lane's FP16 P'^T values (the V tile
                       // holds v + 1152: O^T carries 1152 times the row's sum)
 };
 
-// Iteration c (phase P = c & 3; stage P holds chunk c). On entry S^T(c) is
-// complete. The iteration runs the S^T(c+1) chain with the softmax of chunk c
-// placed between its MFMAs, two scores per MFMA, so the matrix pipe and the
-// VALU work at the same time, and one O^T += V^T P'^T update:
-//   kPvLast = false: chunk c-1's, issued first (its P'^T and V^T operands are
-//     in registers, and it covers the latency of the iteration's LDS reads);
-//   kPvLast = true: chunk c's, issued last, after its P'^T is formed.
-// The two waves that share a SIMD use the two orders, so that one issues its
-// O^T update while the other runs its softmax.
-template <int P, bool kPvLast>
-__device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half8 qf[8],
+// Iteration c (phase P = c & 3). On entry S^T(c) is complete. The iteration
+// runs the S^T(c+1) chain with the softmax of chunk c placed between its MFMAs,
+// two scores per MFMA, so the matrix pipe and the VALU work at the same time,
+// forms P'^T(c), and closes with O^T += V^T P'^T for chunk c.
+template <int P>
+__device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Float16* qrow,
                                              float s_init, int ch, int hb, int l32) {
-  const Stage st = stage(sm, P);
-  const Stage st_next = stage(sm, (P + 1) & 3);
+  const Stage st = stage(sm, P);            // chunk c: factors, chooser bytes, V
+  const Stage st_next = stage(sm, P + 1);   // chunk c+1: K
   const float ninf = -__builtin_inff();
 
-  // LDS reads: chunk c's chooser bytes and k factors
-  const u32x4 em_lo = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch);
-  const u32x4 em_hi = *reinterpret_cast<const u32x4*>(st.emask + 8 * ch + 4);
+  // LDS reads: chunk c's chooser bytes (the four words holding this lane's
+  // cells 32ch + 8q + 4hb + {0..3}, q = 0..3) and k factors
+  uint32_t emw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) emw[q] = st.emask[8 * ch + 2 * q + hb];
   float4v k4[4], v4[4];
   k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
   k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
 
-  // O^T += V^T P'^T of chunk c-1, then the first two of chunk c+1's K operands
-  // (the others are read two MFMAs ahead of their use in the chain below)
-  half8 kfrag[8];
+  // the first two of chunk c+1's K operands and Q's (the others are read two
+  // MFMAs ahead of their use in the chain below)
+  half8 kfrag[8], qfrag[8];
   const int cell = 32 * ch + l32;
-  if (!kPvLast) {
-    const Stage st_prev = stage(sm, (P + 3) & 3);
+  const _Float16* krow = st_next.k + cell * kKRow + 8 * hb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const half8 va = load_v_operand(st_prev, ch, j >> 2, j & 3, (hb << 5) | l32);
-      cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
-    }
+  for (int j = 0; j < 2; ++j) {
+    kfrag[j] = *reinterpret_cast<const half8*>(krow + 16 * j);
+    qfrag[j] = *reinterpret_cast<const half8*>(qrow + 16 * j);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    kfrag[j] = *reinterpret_cast<const half8*>(st_next.k + cell * kKRow + 8 * hb + 16 * j);
-  __builtin_amdgcn_sched_barrier(0);
 
-  // per-score lane masks: the chooser byte replicated over the 8 rows of each
-  // position group (row n's bit is n & 7 = lane & 7)
-  uint32_t em[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    em[k] = __builtin_amdgcn_readfirstlane(em_lo[k]);
-    em[4 + k] = __builtin_amdgcn_readfirstlane(em_hi[k]);
-  }
+  // per-score keep flags: bit (row & 7) = bit (lane & 7) of the cell's chooser
+  // byte (one AND per word with this lane's bit in every byte, one compare per
+  // score)
   bool keep[16];
+  {
+    const uint32_t bitm = (1u << (l32 & 7)) * 0x01010101u;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const uint32_t lo = (em[2 * (r >> 2)] >> (8 * (r & 3))) & 0xffu;
-    const uint32_t hi = (em[2 * (r >> 2) + 1] >> (8 * (r & 3))) & 0xffu;
-    const uint64_t lm = (uint64_t)(lo * 0x01010101u) | ((uint64_t)(hi * 0x01010101u) << 32);
-    keep[r] = __builtin_amdgcn_inverse_ballot_w64(lm);
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = emw[q] & bitm;
+      keep[4 * q + 0] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<0>(w));
+      keep[4 * q + 1] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<1>(w));
+      keep[4 * q + 2] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<2>(w));
+      keep[4 * q + 3] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<3>(w));
+    }
   }
 
   // S^T(c+1) chain, the softmax of chunk c between its MFMAs
@@ -352,9 +360,11 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half
   float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qf[j], s_next, 0, 0, 0);
-    if (j + 2 < 8)
-      kfrag[j + 2] = *reinterpret_cast<const half8*>(st_next.k + cell * kKRow + 8 * hb + 16 * (j + 2));
+    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qfrag[j], s_next, 0, 0, 0);
+    if (j + 2 < 8) {
+      kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
+      qfrag[j + 2] = *reinterpret_cast<const half8*>(qrow + 16 * (j + 2));
+    }
 #pragma unroll
     for (int r = 2 * j; r < 2 * j + 2; ++r) {
       const float u = keep[r] ? __builtin_fmaf(cs.s_cur[r], k4[r >> 2][r & 3], -cs.m_run) : ninf;
@@ -418,31 +428,29 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const half
     cs.lp = lp;
   }
 
-  if (kPvLast) {
+  // O^T += V^T P'^T of chunk c
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const half8 va = load_v_operand(st, ch, j >> 2, j & 3, (hb << 5) | l32);
-      cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
-    }
+  for (int j = 0; j < 8; ++j) {
+    const half8 va = load_v_operand(st, ch, j >> 2, j & 3, (hb << 5) | l32);
+    cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
   }
   cs.s_cur = s_next;
   lds_barrier();
 }
 
-template <bool kPvLast>
-__device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, const half8 qf[8],
+__device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, const _Float16* qrow,
                                                float s_init, int ch, int hb, int l32, int nch) {
   int c = 0;
   for (; c + 4 <= nch; c += 4) {
-    consume_step<0, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
-    consume_step<1, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
-    consume_step<2, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
-    consume_step<3, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+    consume_step<0>(cs, sm, qrow, s_init, ch, hb, l32);
+    consume_step<1>(cs, sm, qrow, s_init, ch, hb, l32);
+    consume_step<2>(cs, sm, qrow, s_init, ch, hb, l32);
+    consume_step<3>(cs, sm, qrow, s_init, ch, hb, l32);
   }
   const int rem = nch - c;
-  if (rem > 0) consume_step<0, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
-  if (rem > 1) consume_step<1, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
-  if (rem > 2) consume_step<2, kPvLast>(cs, sm, qf, s_init, ch, hb, l32);
+  if (rem > 0) consume_step<0>(cs, sm, qrow, s_init, ch, hb, l32);
+  if (rem > 1) consume_step<1>(cs, sm, qrow, s_init, ch, hb, l32);
+  if (rem > 2) consume_step<2>(cs, sm, qrow, s_init, ch, hb, l32);
 }
 
 __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
@@ -459,8 +467,10 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   const int qi = 8 * g + (row_n & 7);
   const bool row_ok = qi < a.n_q;
 
-  // Q^T as the B operand of S^T = K Q^T: k-step s covers dims 16s..16s+15,
-  // this lane holds dims 16s + 8hb .. +7 of its row.
+  // Q in FP16 into the Q tile (the B operand of S^T = K Q^T is read from there:
+  // k-step s covers dims 16s..16s+15, lane half hb dims 16s + 8hb .. +7). Both
+  // waves of a row block convert its rows (for their sums below); the ch = 0
+  // wave stores them.
   half8 qf[8];
   {
     const float* qrow = a.q + ((int64_t)(row_ok ? qi : 0) * n_qh + h * kQPerKv + hq) * kD;
@@ -482,8 +492,13 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) qsum += (float)qf[s][e];
   const float s_init = -1152.f * (qsum + __shfl_xor(qsum, 32));
+  _Float16* qrow = sm.q + row_n * kKRow + 8 * hb;
+  if (ch == 0) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) *reinterpret_cast<half8*>(qrow + 16 * s) = qf[s];
+  }
 
-  lds_barrier();   // prologue: ring filled
+  lds_barrier();   // prologue: ring filled, Q tile stored
   lds_barrier();   // prologue: chunks 0 and 1 staged
 
   ConsState cs;
@@ -494,28 +509,10 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) cs.o[mb][r] = 0.f;
-  // a zero P'^T (with stage 3's V tile zeroed by the producers) for the first
-  // iteration's update of the previous chunk
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) cs.pb[ks][e] = (_Float16)0.f;
-  cs.s_cur = scores_t(stage(sm, 0), qf, ch, hb, l32, s_init);
+  cs.s_cur = scores_t(stage(sm, 0), qrow, ch, hb, l32, s_init);
+  lds_barrier();   // prologue: chunk 0's K tile read (the producers rewrite it next)
 
-  if (wave < 4) {
-    consume_chunks<false>(cs, sm, qf, s_init, ch, hb, l32, nch);
-    // the last chunk's O^T update
-    if (nch > 0) {
-      const Stage st_last = stage(sm, (nch - 1) & 3);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const half8 va = load_v_operand(st_last, ch, j >> 2, j & 3, (hb << 5) | l32);
-        cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
-      }
-    }
-  } else {
-    consume_chunks<true>(cs, sm, qf, s_init, ch, hb, l32, nch);
-  }
+  consume_chunks(cs, sm, qrow, s_init, ch, hb, l32, nch);
   // remove the V tile's offset: 1152 times the row's sum of P'^T values
   {
     const float corr = 1152.f * (cs.lp + __shfl_xor(cs.lp, 32));
@@ -530,7 +527,7 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   lds_barrier();   // every wave is done with the tiles the merge reuses
 
   // ---- merge the two cell halves of each row block and write the output
-  float* xo = reinterpret_cast<float*>(&sm.k[0][0]);   // [3][16 float4 groups][64 lanes][4]
+  float* xo = reinterpret_cast<float*>(&sm.v[0][0]);   // [3][16 float4 groups][64 lanes][4]
   float* xm = xo + 3 * 64 * 64;                      // [3][64]
   float* xl = xm + 3 * 64;                           // [3][64]
   if (ch == 1) {
@@ -648,7 +645,7 @@ __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, Pro
   finish_translation(a, ps.pg[(P + kAheadFinish) & 3], U, cf, h,
                      sm.ring[translator ? (cf & (kRing - 1)) : kRing], lane, flags);
   gather(a, sm.ring[(c + kAheadGather) & (kRing - 1)], ptid, ps.raw[(P + kAheadGather) & 3]);
-  convert(a, stage(sm, (P + 2) & 3), ptid, ps.raw[(P + 2) & 3], flags);
+  convert(a, stage(sm, P + 2), ptid, ps.raw[(P + 2) & 3], flags);
   lds_barrier();
 }
 
@@ -679,13 +676,6 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
     for (int i = 0; i < kAheadFinish; ++i)
       finish_translation(a, p[i], U, i, h, sm.ring[translator ? i : kRing], lane, flags);
   }
-  // stage 3's V tile meets the zero P'^T of the consumers' first update: keep
-  // it finite
-  {
-    u32x4* z = reinterpret_cast<u32x4*>(sm.v[kStages - 1]);
-#pragma unroll
-    for (int i = 0; i < (kD * kChunk * 2) / (16 * 128); ++i) z[ptid + 128 * i] = u32x4{0u, 0u, 0u, 0u};
-  }
   lds_barrier();
 #pragma unroll
   for (int x = 0; x < kAheadGather; ++x) {
@@ -696,6 +686,7 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
   for (int x = (kAheadGather > 4 ? kAheadGather - 4 : 0); x < 2; ++x)
     convert(a, stage(sm, x), ptid, ps.raw[x & 3], flags);
   lds_barrier();
+  lds_barrier();   // the consumers have read chunk 0's K tile
 
   int c = 0;
   for (; c + 4 <= nch; c += 4) {
