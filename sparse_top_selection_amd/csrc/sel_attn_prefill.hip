@@ -78,7 +78,7 @@ struct __align__(16) Ring {
 };
 
 struct __align__(16) Smem {
-  _Float16 k[kKStages][kChunk * kKRow]; // [cell][dim] holding k + 1152, rows of kKRow
+  _Float16 k[kKStages][kChunk * kKRow]; // [cell][dim], rows of kKRow
   _Float16 v[kStages][kChunk * kD];     // [cell][dim], swizzled by v_pos()
   float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
   float vf[kStages][kChunk];            // v_scale * 2^10; 0 where unusable
@@ -118,9 +118,8 @@ __device__ __forceinline__ void lds_barrier() {
 // INT8 -> FP16: bias each byte to unsigned (v + 128) and place it under the
 // FP16 exponent of 1024 (bit pattern 0x64XX = 1024 + XX): the exact FP16 value
 // of v + 1152.
-// four int8 in one dword -> the FP16 bit patterns of k + 1152 (exact), two per
-// dword. The K tile keeps this bias: the S^T accumulator starts at
-// -1152 * sum_d q_d instead of 0, which removes it (see consume()).
+// four int8 in one dword -> the FP16 bit patterns of x + 1152 (exact), two per
+// dword.
 __device__ __forceinline__ uint2 i8x4_to_biased_half(uint32_t w) {
   const uint32_t u = w ^ 0x80808080u;
   return uint2{__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u),
@@ -159,13 +158,20 @@ __device__ __forceinline__ uint32_t task_offset(const Ring& rg, int t) {
   return rg.off[t >> 3] + 16u * (t & 7);
 }
 
+// K is stored as exact FP16 integers (the offset removed with one packed FP16
+// subtraction per pair), so every S^T chain starts from zero.
+__device__ __forceinline__ uint32_t unbias_pair(uint32_t biased) {
+  const half2 h = __builtin_bit_cast(half2, biased) - half2{(_Float16)1152.f, (_Float16)1152.f};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 __device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) {
   const int cell = t >> 3;
   const int u0 = 2 * (t & 7);
   const uint2 b0 = i8x4_to_biased_half(raw.x), b1 = i8x4_to_biased_half(raw.y);
   const uint2 b2 = i8x4_to_biased_half(raw.z), b3 = i8x4_to_biased_half(raw.w);
-  const u32x4 a0 = u32x4{b0.x, b0.y, b1.x, b1.y};
-  const u32x4 a1 = u32x4{b2.x, b2.y, b3.x, b3.y};
+  const u32x4 a0 = u32x4{unbias_pair(b0.x), unbias_pair(b0.y), unbias_pair(b1.x), unbias_pair(b1.y)};
+  const u32x4 a1 = u32x4{unbias_pair(b2.x), unbias_pair(b2.y), unbias_pair(b3.x), unbias_pair(b3.y)};
   _Float16* base = st.k + cell * kKRow + 8 * u0;
   *reinterpret_cast<u32x4*>(base) = a0;
   *reinterpret_cast<u32x4*>(base + 8) = a1;
@@ -246,10 +252,10 @@ __device__ __forceinline__ void finish_translation(const PrefillArgs& a, const P
 // S^T (this wave's 32 cells x 32 rows) of one chunk. qrow: this lane's row of
 // the Q tile, at dims 8hb (k-step ks reads dims 16ks + 8hb .. +7).
 __device__ __forceinline__ float16v scores_t(const Stage& st, const _Float16* qrow, int ch, int hb,
-                                             int l32, float s_init) {
+                                             int l32) {
   float16v s;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = s_init;
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
   const int cell = 32 * ch + l32;
   const _Float16* krow = st.k + cell * kKRow + 8 * hb;
 #pragma unroll
@@ -298,20 +304,23 @@ __device__ __forceinline__ uint64_t byte_nonzero(uint32_t w) {
 struct ConsState {
   float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^10
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
-  half8 pb[2];        // P'^T of the current chunk, once formed
+  half8 pb[2];        // P'^T of the previous chunk
+  half8 vfrag[8];     // V^T operands of the previous chunk
   float m_run;        // running maximum (log2 domain) of this lane's row
   float l_run;        // running sum of probabilities against m_run
   float lp;           // running sum of this lane's FP16 P'^T values (the V tile
                       // holds v + 1152: O^T carries 1152 times the row's sum)
 };
 
-// Iteration c (phase P = c & 3). On entry S^T(c) is complete. The iteration
-// runs the S^T(c+1) chain with the softmax of chunk c placed between its MFMAs,
-// two scores per MFMA, so the matrix pipe and the VALU work at the same time,
-// forms P'^T(c), and closes with O^T += V^T P'^T for chunk c.
+// Iteration c (phase P = c & 3). On entry S^T(c) is complete and chunk c-1's
+// P'^T and V^T operands are in registers. The iteration issues O^T += V^T P'^T
+// for chunk c-1, runs the S^T(c+1) chain with the softmax of chunk c placed
+// between its MFMAs, two scores per MFMA, so the matrix pipe and the VALU work
+// at the same time, forms P'^T(c) and reads chunk c's V^T operands (their LDS
+// latency passes during the barrier).
 template <int P>
 __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Float16* qrow,
-                                             float s_init, int ch, int hb, int l32) {
+                                             int ch, int hb, int l32) {
   const Stage st = stage(sm, P);            // chunk c: factors, chooser bytes, V
   const Stage st_next = stage(sm, P + 1);   // chunk c+1: K
   const float ninf = -__builtin_inff();
@@ -324,6 +333,11 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   float4v k4[4], v4[4];
   k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
   k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
+
+  // O^T += V^T P'^T of chunk c-1
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[j], cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
 
   // the first two of chunk c+1's K operands and Q's (the others are read two
   // MFMAs ahead of their use in the chain below)
@@ -355,7 +369,7 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   // S^T(c+1) chain, the softmax of chunk c between its MFMAs
   float16v s_next;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s_next[r] = s_init;
+  for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
   float pr[16];
   float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
@@ -428,29 +442,27 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
     cs.lp = lp;
   }
 
-  // O^T += V^T P'^T of chunk c
+  // chunk c's V^T operands for the next iteration's update (stage c & 3 is
+  // rewritten only three iterations from now)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const half8 va = load_v_operand(st, ch, j >> 2, j & 3, (hb << 5) | l32);
-    cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
-  }
+  for (int j = 0; j < 8; ++j) cs.vfrag[j] = load_v_operand(st, ch, j >> 2, j & 3, (hb << 5) | l32);
   cs.s_cur = s_next;
   lds_barrier();
 }
 
 __device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, const _Float16* qrow,
-                                               float s_init, int ch, int hb, int l32, int nch) {
+                                               int ch, int hb, int l32, int nch) {
   int c = 0;
   for (; c + 4 <= nch; c += 4) {
-    consume_step<0>(cs, sm, qrow, s_init, ch, hb, l32);
-    consume_step<1>(cs, sm, qrow, s_init, ch, hb, l32);
-    consume_step<2>(cs, sm, qrow, s_init, ch, hb, l32);
-    consume_step<3>(cs, sm, qrow, s_init, ch, hb, l32);
+    consume_step<0>(cs, sm, qrow, ch, hb, l32);
+    consume_step<1>(cs, sm, qrow, ch, hb, l32);
+    consume_step<2>(cs, sm, qrow, ch, hb, l32);
+    consume_step<3>(cs, sm, qrow, ch, hb, l32);
   }
   const int rem = nch - c;
-  if (rem > 0) consume_step<0>(cs, sm, qrow, s_init, ch, hb, l32);
-  if (rem > 1) consume_step<1>(cs, sm, qrow, s_init, ch, hb, l32);
-  if (rem > 2) consume_step<2>(cs, sm, qrow, s_init, ch, hb, l32);
+  if (rem > 0) consume_step<0>(cs, sm, qrow, ch, hb, l32);
+  if (rem > 1) consume_step<1>(cs, sm, qrow, ch, hb, l32);
+  if (rem > 2) consume_step<2>(cs, sm, qrow, ch, hb, l32);
 }
 
 __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
@@ -468,34 +480,20 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   const bool row_ok = qi < a.n_q;
 
   // Q in FP16 into the Q tile (the B operand of S^T = K Q^T is read from there:
-  // k-step s covers dims 16s..16s+15, lane half hb dims 16s + 8hb .. +7). Both
-  // waves of a row block convert its rows (for their sums below); the ch = 0
-  // wave stores them.
-  half8 qf[8];
-  {
-    const float* qrow = a.q + ((int64_t)(row_ok ? qi : 0) * n_qh + h * kQPerKv + hq) * kD;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      float4v x0 = *reinterpret_cast<const float4v*>(qrow + 16 * s + 8 * hb);
-      float4v x1 = *reinterpret_cast<const float4v*>(qrow + 16 * s + 8 * hb + 4);
-      if (!row_ok) x0 = x1 = float4v{0.f, 0.f, 0.f, 0.f};
-      qf[s] = half8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
-                    (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
-    }
-  }
-
-  // the K tile holds k + 1152: start every S^T accumulator at -1152 * sum_d q_d
-  // of this lane's row (its 64 dims here, the other 64 in lane ^ 32)
-  float qsum = 0.f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qsum += (float)qf[s][e];
-  const float s_init = -1152.f * (qsum + __shfl_xor(qsum, 32));
+  // k-step s covers dims 16s..16s+15, lane half hb dims 16s + 8hb .. +7); the
+  // ch = 0 wave of each row block stores its rows.
   _Float16* qrow = sm.q + row_n * kKRow + 8 * hb;
   if (ch == 0) {
+    const float* qg = a.q + ((int64_t)(row_ok ? qi : 0) * n_qh + h * kQPerKv + hq) * kD;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) *reinterpret_cast<half8*>(qrow + 16 * s) = qf[s];
+    for (int s = 0; s < 8; ++s) {
+      float4v x0 = *reinterpret_cast<const float4v*>(qg + 16 * s + 8 * hb);
+      float4v x1 = *reinterpret_cast<const float4v*>(qg + 16 * s + 8 * hb + 4);
+      if (!row_ok) x0 = x1 = float4v{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<half8*>(qrow + 16 * s) =
+          half8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+    }
   }
 
   lds_barrier();   // prologue: ring filled, Q tile stored
@@ -509,10 +507,22 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) cs.o[mb][r] = 0.f;
-  cs.s_cur = scores_t(stage(sm, 0), qrow, ch, hb, l32, s_init);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs.vfrag[j][e] = (_Float16)0.f;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs.pb[ks][e] = (_Float16)0.f;
+  cs.s_cur = scores_t(stage(sm, 0), qrow, ch, hb, l32);
   lds_barrier();   // prologue: chunk 0's K tile read (the producers rewrite it next)
 
-  consume_chunks(cs, sm, qrow, s_init, ch, hb, l32, nch);
+  consume_chunks(cs, sm, qrow, ch, hb, l32, nch);
+  // the last chunk's O^T update
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[j], cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
   // remove the V tile's offset: 1152 times the row's sum of P'^T values
   {
     const float corr = 1152.f * (cs.lp + __shfl_xor(cs.lp, 32));
