@@ -14,30 +14,37 @@
 //   * one 512-thread workgroup (8 wave64s, one per CU at this register budget,
 //     two per SIMD) per (group g, KV head h); grid order is XCD-aware so that
 //     each XCD walks consecutive groups of one KV head;
-//   * waves 0..5 consume, waves 6..7 produce. The producers translate union
-//     cells through the page table, gather the INT8 K/V rows with 16-byte /
-//     8-byte loads two chunks ahead of their use, convert them to FP16 and store
-//     them into a 4-stage LDS ring of tiles; the consumers only read LDS;
+//   * waves 0..5 consume, waves 6..7 produce (at raised priority: every wave
+//     waits for their stage at the barrier). The producers translate union
+//     cells through the page table and gather the INT8 K/V rows with 16-byte
+//     loads, every read consumed kLead iterations after it was issued, convert
+//     the rows to FP16 and store them into LDS (K tiles in two stages, V tiles
+//     and per-cell factors in four); the consumers only read LDS;
 //   * row n of the 96 = 8*hq + i (query head h*12+hq, position 8g+i), so the
 //     chooser bit of row n is n & 7; consumer wave w owns row block rb = w % 3
 //     (32 rows) and cell half ch = w / 3 (32 of each chunk's 64 cells) with its
 //     own softmax state; the two halves are merged once at the end;
-//   * S^T (32 cells x 32 rows, K=128) is 8 v_mfma_f32_32x32x16_f16 from the LDS K
-//     tile with Q^T held in registers; O^T (128 dims x 32 rows) += V^T P^T is 8
-//     more MFMAs whose B operand (P^T) comes straight from the S^T accumulator
-//     registers: the V^T tile is stored in the matching cell permutation;
-//   * each consumer iteration issues the MFMAs of S^T for chunk c+1 and of
-//     O^T += V^T P^T for chunk c-1, interleaved with the softmax of chunk c, so
-//     the matrix pipe and the VALU work at the same time;
+//   * S^T (32 cells x 32 rows, K=128) is 8 v_mfma_f32_32x32x16_f16 from the K
+//     tile and the work-group's Q tile (both in LDS); O^T (128 dims x 32 rows)
+//     += V^T P'^T is 8 more MFMAs whose B operand (P'^T) comes straight from
+//     the S^T accumulator registers, and whose A operand is read transposed
+//     from the [cell][dim] V tile (ds_read_b64_tr_b16) in the same cell order;
+//   * each consumer iteration issues the O^T update of chunk c-1, then the
+//     S^T(c+1) chain with the softmax of chunk c between its MFMAs, so the
+//     matrix pipe and the VALU work at the same time;
 //   * K and V integers are exact in FP16, so the scales are applied in FP32:
 //     k_scale * softmax_scale * log2(e) multiplies the score, v_scale * 2^10 the
-//     probability before its FP16 rounding (2^-10 returns in the epilogue);
-//   * the chooser byte of a cell becomes a 64-bit SGPR lane mask (the byte
-//     replicated 4x per 32 lanes) and one v_cndmask applies it per score;
+//     probability before its FP16 rounding (2^-10 returns in the epilogue). The
+//     V tile keeps the +1152 offset of the byte-to-FP16 trick; each lane tracks
+//     the sum of the FP16 probabilities it feeds the MFMA and 1152 times that
+//     sum is removed once at the end;
+//   * a lane's 16 keep flags come from its cells' chooser bytes: one AND with
+//     the lane's bit in every byte, one byte-select compare per score; one
+//     v_cndmask applies each;
 //   * online softmax with a lazy stabiliser: probabilities are taken against
 //     the running maximum, and only when a lane's chunk sum exceeds 16 does the
-//     wave recompute the chunk maximum and rescale O and l (always on a row's
-//     first chosen chunk, rarely after).
+//     wave recompute the chunk maximum and rescale O, l and the probability sum
+//     (always on a row's first chosen chunk, rarely after).
 
 #include "sel_attn_internal.h"
 
@@ -580,11 +587,13 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 
 // ---------------------------------------------------------------------------
 // Producer waves 6..7 (128 threads, ptid = tid - 384). Iteration c (while the
-// consumers work on chunks c and c+1): translate chunk c+4 (union entry read two
-// iterations earlier, page entry one), gather chunk c+3 into registers, convert
-// chunk c+2 (gathered one iteration earlier) into its LDS stage. Each thread
-// owns tasks ptid + 128k (k = 0..3) of both pools, and the k scale (ptid < 64)
-// or v scale of cell ptid & 63; wave 6 translates.
+// consumers work on chunks c and c+1): read the union entries of chunk
+// c+kAheadUnion, the page-table entries of chunk c+kAheadPage, publish the
+// pool rows of chunk c+kAheadFinish in the ring, gather chunk c+kAheadGather
+// into registers and convert chunk c+2 (gathered kLead iterations earlier) into
+// its LDS stages. Each thread owns tasks ptid + 128k (k = 0..3) of both pools,
+// and the k scale (ptid < 64) or v scale of cell ptid & 63; both waves
+// translate the same lanes, wave 6 into the ring.
 struct Raw {
   u32x4 k[4];
   u32x4 v[4];
