@@ -319,6 +319,47 @@ struct ConsState {
                       // holds v + 1152: O^T carries 1152 times the row's sum)
 };
 
+// The S^T(c+1) chain with the softmax of chunk c between its MFMAs (two scores
+// per MFMA); K and Q operands are read two MFMAs ahead, the remaining k factors
+// and the v factors on the way. Returns this lane's probability sum.
+template <bool kMasked>
+__device__ __forceinline__ float chain_softmax(const ConsState& cs, const Stage& st,
+                                               const _Float16* krow, const _Float16* qrow,
+                                               const bool keep[16], half8 kfrag[8], half8 qfrag[8],
+                                               float4v k4[4], float4v v4[4], float16v& s_next,
+                                               float pr[16], int ch, int hb) {
+  const float ninf = -__builtin_inff();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
+  float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qfrag[j], s_next, 0, 0, 0);
+    if (j + 2 < 8) {
+      kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
+      qfrag[j + 2] = *reinterpret_cast<const half8*>(qrow + 16 * (j + 2));
+    }
+#pragma unroll
+    for (int r = 2 * j; r < 2 * j + 2; ++r) {
+      const float u = __builtin_fmaf(cs.s_cur[r], k4[r >> 2][r & 3], -cs.m_run);
+      pr[r] = __builtin_amdgcn_exp2f(kMasked ? (keep[r] ? u : ninf) : u);
+    }
+    psum0 += pr[2 * j];
+    psum1 += pr[2 * j + 1];
+    if (j == 1 || j == 3) {   // k factors two MFMAs ahead of their scores
+      const int q4 = (j + 3) >> 1;
+      k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+    }
+    if (j == 5) {   // v factors, into registers the first K operands held
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return psum0 + psum1;
+}
+
 // Iteration c (phase P = c & 3). On entry S^T(c) is complete and chunk c-1's
 // P'^T and V^T operands are in registers. The iteration issues O^T += V^T P'^T
 // for chunk c-1, runs the S^T(c+1) chain with the softmax of chunk c placed
@@ -359,9 +400,20 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
 
   // per-score keep flags: bit (row & 7) = bit (lane & 7) of the cell's chooser
   // byte (one AND per word with this lane's bit in every byte, one compare per
-  // score)
+  // score). When all 32 cells of this wave's half are chosen by all 8 positions
+  // (most chunks of blocks every position keeps) the flags are all set and the
+  // softmax runs without them.
+  const bool all_chosen =
+      __builtin_amdgcn_ballot_w64((emw[0] & emw[1] & emw[2] & emw[3]) != 0xffffffffu) == 0;
   bool keep[16];
-  {
+  float16v s_next;
+  float pr[16];
+  float psum;
+  if (all_chosen) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) keep[r] = true;
+    psum = chain_softmax<false>(cs, st, krow, qrow, keep, kfrag, qfrag, k4, v4, s_next, pr, ch, hb);
+  } else {
     const uint32_t bitm = (1u << (l32 & 7)) * 0x01010101u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -371,40 +423,8 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
       keep[4 * q + 2] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<2>(w));
       keep[4 * q + 3] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<3>(w));
     }
+    psum = chain_softmax<true>(cs, st, krow, qrow, keep, kfrag, qfrag, k4, v4, s_next, pr, ch, hb);
   }
-
-  // S^T(c+1) chain, the softmax of chunk c between its MFMAs
-  float16v s_next;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
-  float pr[16];
-  float psum0 = 0.f, psum1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qfrag[j], s_next, 0, 0, 0);
-    if (j + 2 < 8) {
-      kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
-      qfrag[j + 2] = *reinterpret_cast<const half8*>(qrow + 16 * (j + 2));
-    }
-#pragma unroll
-    for (int r = 2 * j; r < 2 * j + 2; ++r) {
-      const float u = keep[r] ? __builtin_fmaf(cs.s_cur[r], k4[r >> 2][r & 3], -cs.m_run) : ninf;
-      pr[r] = __builtin_amdgcn_exp2f(u);
-    }
-    psum0 += pr[2 * j];
-    psum1 += pr[2 * j + 1];
-    if (j == 1 || j == 3) {   // k factors two MFMAs ahead of their scores
-      const int q4 = (j + 3) >> 1;
-      k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
-    }
-    if (j == 5) {   // v factors, into registers the first K operands held
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  float psum = psum0 + psum1;
 
   // the lazy stabiliser: only when some lane's chunk sum leaves (0, 16] is the
   // running maximum moved (what is accumulated is rescaled; this waits for the
