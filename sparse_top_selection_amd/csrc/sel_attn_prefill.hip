@@ -72,8 +72,8 @@ constexpr int kLead = 3;            // iterations between a read and its first u
 constexpr int kRing = 8;            // translated chunks (ring slots, indexed by chunk & 7)
 constexpr float kLazyLimit = 16.f;
 constexpr float kNoMax = -1e30f;    // stabiliser before a row has seen a chosen cell
-constexpr float kVFold = 1024.f;    // probabilities carry v_scale * 2^10 into FP16
-constexpr float kVScaleLimit = 4.f;
+constexpr float kVFold = 512.f;     // the FP16 v factor is v_scale * 2^9
+constexpr float kVScaleLimit = 4.f; // so that v factor (< 2^11) times probability (<= 16) fits FP16
 
 // LDS: the four stages' K tiles, then their V tiles, so that a stage's tile
 // addresses differ by multiples of the tile size that fit the 16-bit immediate
@@ -88,9 +88,8 @@ struct __align__(16) Smem {
   _Float16 k[kKStages][kChunk * kKRow]; // [cell][dim], rows of kKRow
   _Float16 v[kStages][kChunk * kD];     // [cell][dim], swizzled by v_pos()
   float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
-  float vf[kStages][kChunk];            // v_scale * 2^10; 0 where unusable
-  uint32_t emask[kStages][kChunk / 4];  // chooser bytes, 0 for padding / non-resident cells
-  uint32_t emask_spare[kStages][kChunk / 4];  // written by the producer wave that owns vf
+  _Float16 vf[kStages][kChunk];         // FP16(v_scale * 2^9); 0 where unusable
+  uint32_t keep[kStages][4 * kChunk];   // keep masks, 16-byte units laid out by keep_unit()
   _Float16 q[kRows * kKRow];            // the work-group's Q, [row][dim] in FP16, rows of kKRow
   Ring ring[kRing + 1];   // the last slot takes the second producer wave's copies
 };
@@ -100,14 +99,24 @@ struct Stage {
   _Float16* k;
   _Float16* v;
   float* kf;
-  float* vf;
-  uint32_t* emask;
-  uint32_t* emask_spare;
+  _Float16* vf;
+  uint32_t* keep;
 };
 
 __device__ __forceinline__ Stage stage(Smem& sm, int c) {
   const int s = c & (kStages - 1);
-  return Stage{sm.k[c & (kKStages - 1)], sm.v[s], sm.kf[s], sm.vf[s], sm.emask[s], sm.emask_spare[s]};
+  return Stage{sm.k[c & (kKStages - 1)], sm.v[s], sm.kf[s], sm.vf[s], sm.keep[s]};
+}
+
+// Keep masks of a chunk: for position bit b (row & 7), cell half ch and lane
+// half hb, eight words; word 2q + j holds in its low and high 16 bits all-ones
+// or zero for cells 32ch + 8q + 4hb + 2j and +1 (the cells, in order, whose
+// scores a consumer lane packs into its j-th probability pair of group q).
+// Words 4u..4u+3 form 16-byte unit keep_unit(b, ch, hb, u): the eight position
+// bits of a unit are adjacent, so the eight rows of a lane octet read eight
+// distinct bank groups.
+__device__ __forceinline__ int keep_unit(int b, int ch, int hb, int u) {
+  return ((2 * ch + hb) * 2 + u) * 8 + b;
 }
 
 // ---------------------------------------------------------------------------
@@ -119,6 +128,17 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The consumers' iteration barrier. A consumer wave writes no LDS inside its
+// loop, and the only LDS reads it may still have in flight here are of a V tile
+// that the producers rewrite two barriers later (by then the reads have been
+// consumed), so it need not wait for them: the barrier only keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void consumer_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -134,35 +154,40 @@ __device__ __forceinline__ uint2 i8x4_to_biased_half(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layouts. Both are XOR-swizzled in 16-byte units so that the
-// producers' stores and the consumers' MFMA-operand loads are free of bank
-// conflicts (8 consecutive lanes always touch 8 distinct units of a 128-byte
-// bank period).
+// LDS tile layouts, chosen so that the producers' 16-byte stores and the
+// consumers' MFMA-operand loads are free of bank conflicts (each lane octet
+// of a 16-byte access touches 8 distinct units of a 128-byte bank period).
 //
 // K tile [cell][dim], rows of 272 bytes (128 dims + 16 bytes of padding): the
 // 16 consecutive cells a consumer half-wave reads at one 16-byte unit fall on
-// 16 distinct bank groups, and so do the two cells x eight even (or odd) units
-// that 16 producer lanes store; every consumer K address is one base plus an
-// immediate.
+// 16 distinct bank groups; a producer octet stores units 2p (then 2p + 1),
+// p = 0..3 or 4..7, of an even cell and the odd cell after it, 17 units
+// apart. Every consumer K address is one base plus an immediate.
 // V tile [cell][dim], rows of 256 bytes, unit u of cell c at u ^ vswz(c),
-// vswz(c) = ((c & 3) << 2) | (c & 1). Producers store units 2p and 2p+1 of one
-// cell per 8 lanes (16 lanes: two cells of opposite parity, even and odd
-// positions); consumers read it transposed, 8 bytes per lane, four
-// consecutive cells x 64 bytes per 32 lanes (4(mb ^ x) + (v ^ (x & 1)) are 16
-// distinct positions). Both are free of bank conflicts.
+// vswz(c) = ((c & 3) << 2) | (c & 1). A producer octet stores the same units
+// as for K, the odd cell's moved by 5 modulo 8; consumers read it transposed,
+// 8 bytes per lane, four consecutive cells x 64 bytes per 32 lanes
+// (4(mb ^ x) + (v ^ (x & 1)) are 16 distinct positions).
 __device__ __forceinline__ int v_pos(int u, int cell) {
   return u ^ (((cell & 3) << 2) | (cell & 1));
 }
 
 // ---------------------------------------------------------------------------
-// Producer staging tasks. Task t in [0,512): cell t>>3, dims 16*(t&7)..+15, one
-// 16-byte load from the K pool and one from the V pool at the same offset.
+// Producer staging tasks. Task t in [0,512) covers cell task_cell(t), dims
+// 16 task_block(t) .. +15: one 16-byte load from the K pool and one from the
+// V pool at the same offset. Each lane octet takes blocks 0..3 (or 4..7) of an
+// even cell and of the odd cell after it, so that its 16-byte stores fall on
+// eight distinct bank groups in both tiles: even and odd rows of the K tile
+// are 17 units apart, and the V swizzle moves odd cells by 5 units (mod 8).
 // Unusable cells (padding, non-resident, bad) read pool row 0, which always
 // exists; their chooser byte and scales are 0, so the values never count.
 // A scale is zeroed exactly when its cell's chooser byte is 0 (such a cell
 // contributes nothing either way).
+__device__ __forceinline__ int task_cell(int t) { return 2 * (t >> 4) + ((t >> 2) & 1); }
+__device__ __forceinline__ int task_block(int t) { return 4 * ((t >> 3) & 1) + (t & 3); }
+
 __device__ __forceinline__ uint32_t task_offset(const Ring& rg, int t) {
-  return rg.off[t >> 3] + 16u * (t & 7);
+  return rg.off[task_cell(t)] + 16u * task_block(t);
 }
 
 // K is stored as exact FP16 integers (the offset removed with one packed FP16
@@ -173,8 +198,8 @@ __device__ __forceinline__ uint32_t unbias_pair(uint32_t biased) {
 }
 
 __device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) {
-  const int cell = t >> 3;
-  const int u0 = 2 * (t & 7);
+  const int cell = task_cell(t);
+  const int u0 = 2 * task_block(t);
   const uint2 b0 = i8x4_to_biased_half(raw.x), b1 = i8x4_to_biased_half(raw.y);
   const uint2 b2 = i8x4_to_biased_half(raw.z), b3 = i8x4_to_biased_half(raw.w);
   const u32x4 a0 = u32x4{unbias_pair(b0.x), unbias_pair(b0.y), unbias_pair(b1.x), unbias_pair(b1.y)};
@@ -187,8 +212,8 @@ __device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) 
 // The V tile keeps v + 1152 too: the consumers track the sum of the FP16
 // probabilities they multiply with it and remove 1152 times that sum at the end.
 __device__ __forceinline__ void store_v_task(const Stage& st, int t, u32x4 raw) {
-  const int cell = t >> 3;
-  const int u0 = 2 * (t & 7);
+  const int cell = task_cell(t);
+  const int u0 = 2 * task_block(t);
   const uint2 b0 = i8x4_to_biased_half(raw.x), b1 = i8x4_to_biased_half(raw.y);
   const uint2 b2 = i8x4_to_biased_half(raw.z), b3 = i8x4_to_biased_half(raw.w);
   _Float16* base = st.v + cell * kD;
@@ -296,20 +321,9 @@ __device__ __forceinline__ half8 load_v_operand(const Stage& st, int ch, int ks,
                (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
 }
 
-// Lane mask of the lanes whose byte E of w is nonzero: one VALU compare with a
-// byte-select operand (the compiler would spend an AND and a compare).
-template <int E>
-__device__ __forceinline__ uint64_t byte_nonzero(uint32_t w) {
-  uint64_t m;
-  asm("v_cmp_ne_u32_sdwa %0, %1, %2 src0_sel:BYTE_%3 src1_sel:DWORD"
-      : "=s"(m)
-      : "v"(w), "v"(0u), "n"(E));
-  return m;
-}
-
 // Registers a consumer wave carries from one iteration to the next.
 struct ConsState {
-  float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^10
+  float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^9
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
   half8 pb[2];        // P'^T of the previous chunk
   half8 vfrag[8];     // V^T operands of the previous chunk
@@ -319,19 +333,40 @@ struct ConsState {
                       // holds v + 1152: O^T carries 1152 times the row's sum)
 };
 
-// The S^T(c+1) chain with the softmax of chunk c between its MFMAs (two scores
-// per MFMA); K and Q operands are read two MFMAs ahead, the remaining k factors
-// and the v factors on the way. Returns this lane's probability sum.
-template <bool kMasked>
-__device__ __forceinline__ float chain_softmax(const ConsState& cs, const Stage& st,
-                                               const _Float16* krow, const _Float16* qrow,
-                                               const bool keep[16], half8 kfrag[8], half8 qfrag[8],
-                                               float4v k4[4], float4v v4[4], float16v& s_next,
-                                               float pr[16], int ch, int hb) {
-  const float ninf = -__builtin_inff();
+// Per-chunk operands of a lane's softmax: k factors of its 16 cells, v factors
+// and keep masks of its 8 cell pairs.
+struct ChunkFactors {
+  float4v k4[4];
+  half2 vf[8];
+  uint32_t keep[8];
+};
+
+// Probability pair j (scores 2j, 2j+1) of chunk c: FP16, masked, summed into
+// psum; times the v factors into P'^T, summed into lpc.
+__device__ __forceinline__ void prob_pair(ConsState& cs, const ChunkFactors& f, int j, float u0,
+                                          float u1, float& psum, float& lpc) {
+  const half2 one = {(_Float16)1.f, (_Float16)1.f};
+  const half2 p = {(_Float16)__builtin_amdgcn_exp2f(u0), (_Float16)__builtin_amdgcn_exp2f(u1)};
+  const half2 pm = __builtin_bit_cast(half2, __builtin_bit_cast(uint32_t, p) & f.keep[j]);
+  psum = __builtin_amdgcn_fdot2(pm, one, psum, false);
+  const half2 pv = pm * f.vf[j];
+  lpc = __builtin_amdgcn_fdot2(pv, one, lpc, false);
+  cs.pb[j >> 2][2 * (j & 3)] = pv[0];
+  cs.pb[j >> 2][2 * (j & 3) + 1] = pv[1];
+}
+
+// The S^T(c+1) chain with the softmax of chunk c between its MFMAs (one
+// probability pair per MFMA); K and Q operands are read two MFMAs ahead, the
+// remaining k factors on the way. Leaves P'^T(c) in cs.pb and returns this
+// lane's probability sum and P'^T sum.
+__device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, const _Float16* krow,
+                                              const _Float16* qrow, ChunkFactors& f,
+                                              half8 kfrag[8], half8 qfrag[8], float16v& s_next,
+                                              float& psum, float& lpc, int ch, int hb) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
-  float psum0 = 0.f, psum1 = 0.f;
+  psum = 0.f;
+  lpc = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qfrag[j], s_next, 0, 0, 0);
@@ -339,48 +374,47 @@ __device__ __forceinline__ float chain_softmax(const ConsState& cs, const Stage&
       kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
       qfrag[j + 2] = *reinterpret_cast<const half8*>(qrow + 16 * (j + 2));
     }
-#pragma unroll
-    for (int r = 2 * j; r < 2 * j + 2; ++r) {
-      const float u = __builtin_fmaf(cs.s_cur[r], k4[r >> 2][r & 3], -cs.m_run);
-      pr[r] = __builtin_amdgcn_exp2f(kMasked ? (keep[r] ? u : ninf) : u);
-    }
-    psum0 += pr[2 * j];
-    psum1 += pr[2 * j + 1];
+    const int r = 2 * j;
+    prob_pair(cs, f, j, __builtin_fmaf(cs.s_cur[r], f.k4[r >> 2][r & 3], -cs.m_run),
+              __builtin_fmaf(cs.s_cur[r + 1], f.k4[r >> 2][(r + 1) & 3], -cs.m_run), psum, lpc);
     if (j == 1 || j == 3) {   // k factors two MFMAs ahead of their scores
       const int q4 = (j + 3) >> 1;
-      k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
-    }
-    if (j == 5) {   // v factors, into registers the first K operands held
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        v4[q4] = *reinterpret_cast<const float4v*>(st.vf + 32 * ch + 8 * q4 + 4 * hb);
+      f.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  return psum0 + psum1;
 }
 
 // Iteration c (phase P = c & 3). On entry S^T(c) is complete and chunk c-1's
 // P'^T and V^T operands are in registers. The iteration issues O^T += V^T P'^T
 // for chunk c-1, runs the S^T(c+1) chain with the softmax of chunk c placed
-// between its MFMAs, two scores per MFMA, so the matrix pipe and the VALU work
-// at the same time, forms P'^T(c) and reads chunk c's V^T operands (their LDS
-// latency passes during the barrier).
+// between its MFMAs, one probability pair per MFMA, so the matrix pipe and the
+// VALU work at the same time, forms P'^T(c) and reads chunk c's V^T operands
+// (their LDS latency passes during the barrier).
 template <int P>
 __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Float16* qrow,
                                              int ch, int hb, int l32) {
-  const Stage st = stage(sm, P);            // chunk c: factors, chooser bytes, V
+  const Stage st = stage(sm, P);            // chunk c: factors, keep masks, V
   const Stage st_next = stage(sm, P + 1);   // chunk c+1: K
   const float ninf = -__builtin_inff();
 
-  // LDS reads: chunk c's chooser bytes (the four words holding this lane's
-  // cells 32ch + 8q + 4hb + {0..3}, q = 0..3) and k factors
-  uint32_t emw[4];
+  // LDS reads: chunk c's keep masks and v factors of this lane's cell pairs,
+  // the first k factors
+  ChunkFactors f;
+  {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(st.keep);
+    const u32x4 a0 = kp[keep_unit(l32 & 7, ch, hb, 0)], a1 = kp[keep_unit(l32 & 7, ch, hb, 1)];
+    f.keep[0] = a0.x; f.keep[1] = a0.y; f.keep[2] = a0.z; f.keep[3] = a0.w;
+    f.keep[4] = a1.x; f.keep[5] = a1.y; f.keep[6] = a1.z; f.keep[7] = a1.w;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) emw[q] = st.emask[8 * ch + 2 * q + hb];
-  float4v k4[4], v4[4];
-  k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
-  k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
+    for (int q = 0; q < 4; ++q) {
+      const half4 v = *reinterpret_cast<const half4*>(st.vf + 32 * ch + 8 * q + 4 * hb);
+      f.vf[2 * q] = half2{v[0], v[1]};
+      f.vf[2 * q + 1] = half2{v[2], v[3]};
+    }
+  }
+  f.k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
+  f.k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
 
   // O^T += V^T P'^T of chunk c-1
 #pragma unroll
@@ -398,42 +432,20 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
     qfrag[j] = *reinterpret_cast<const half8*>(qrow + 16 * j);
   }
 
-  // per-score keep flags: bit (row & 7) = bit (lane & 7) of the cell's chooser
-  // byte (one AND per word with this lane's bit in every byte, one compare per
-  // score). When all 32 cells of this wave's half are chosen by all 8 positions
-  // (most chunks of blocks every position keeps) the flags are all set and the
-  // softmax runs without them.
-  const bool all_chosen =
-      __builtin_amdgcn_ballot_w64((emw[0] & emw[1] & emw[2] & emw[3]) != 0xffffffffu) == 0;
-  bool keep[16];
   float16v s_next;
-  float pr[16];
-  float psum;
-  if (all_chosen) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) keep[r] = true;
-    psum = chain_softmax<false>(cs, st, krow, qrow, keep, kfrag, qfrag, k4, v4, s_next, pr, ch, hb);
-  } else {
-    const uint32_t bitm = (1u << (l32 & 7)) * 0x01010101u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w = emw[q] & bitm;
-      keep[4 * q + 0] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<0>(w));
-      keep[4 * q + 1] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<1>(w));
-      keep[4 * q + 2] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<2>(w));
-      keep[4 * q + 3] = __builtin_amdgcn_inverse_ballot_w64(byte_nonzero<3>(w));
-    }
-    psum = chain_softmax<true>(cs, st, krow, qrow, keep, kfrag, qfrag, k4, v4, s_next, pr, ch, hb);
-  }
+  float psum, lpc;
+  chain_softmax(cs, st, krow, qrow, f, kfrag, qfrag, s_next, psum, lpc, ch, hb);
 
-  // the lazy stabiliser: only when some lane's chunk sum leaves (0, 16] is the
+  // the lazy stabiliser: only when some lane's chunk sum leaves [0, 16] is the
   // running maximum moved (what is accumulated is rescaled; this waits for the
   // MFMAs issued above) and the chunk redone against it
   if (__ballot(!(psum <= kLazyLimit))) {
     float cmax = ninf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      cmax = fmaxf(cmax, keep[r] ? cs.s_cur[r] * k4[r >> 2][r & 3] : ninf);
+    for (int r = 0; r < 16; ++r) {
+      const bool keep = (f.keep[r >> 1] >> (16 * (r & 1))) & 1u;
+      cmax = fmaxf(cmax, keep ? cs.s_cur[r] * f.k4[r >> 2][r & 3] : ninf);
+    }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
     const float m_new = fmaxf(cs.m_run, cmax);
     const float alpha = __builtin_amdgcn_exp2f(cs.m_run - m_new);
@@ -445,36 +457,23 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
 #pragma unroll
       for (int r = 0; r < 16; ++r) cs.o[mb][r] *= alpha;
     psum = 0.f;
+    lpc = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float u = keep[r] ? __builtin_fmaf(cs.s_cur[r], k4[r >> 2][r & 3], -cs.m_run) : ninf;
-      pr[r] = __builtin_amdgcn_exp2f(u);
-      psum += pr[r];
+    for (int j = 0; j < 8; ++j) {
+      const int r = 2 * j;
+      prob_pair(cs, f, j, __builtin_fmaf(cs.s_cur[r], f.k4[r >> 2][r & 3], -cs.m_run),
+                __builtin_fmaf(cs.s_cur[r + 1], f.k4[r >> 2][(r + 1) & 3], -cs.m_run), psum, lpc);
     }
   }
   cs.l_run += psum;
-
-  // P'^T of chunk c (probabilities times v_scale * 2^10, in FP16), the B
-  // operand of the next iteration's O^T update
-#pragma unroll
-  for (int r = 0; r < 16; ++r) cs.pb[r >> 3][r & 7] = (_Float16)(pr[r] * v4[r >> 2][r & 3]);
-  {
-    const half2 one = {(_Float16)1.f, (_Float16)1.f};
-    float lp = cs.lp;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const half2 pair = {cs.pb[k >> 2][2 * (k & 3)], cs.pb[k >> 2][2 * (k & 3) + 1]};
-      lp = __builtin_amdgcn_fdot2(pair, one, lp, false);
-    }
-    cs.lp = lp;
-  }
+  cs.lp += lpc;
 
   // chunk c's V^T operands for the next iteration's update (stage c & 3 is
   // rewritten only three iterations from now)
 #pragma unroll
   for (int j = 0; j < 8; ++j) cs.vfrag[j] = load_v_operand(st, ch, j >> 2, j & 3, (hb << 5) | l32);
   cs.s_cur = s_next;
-  lds_barrier();
+  consumer_barrier();
 }
 
 __device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, const _Float16* qrow,
@@ -619,7 +618,16 @@ struct Raw {
   u32x4 v[4];
   float sc;     // k scale (wave 6) or v scale (wave 7) of cell ptid & 63 (row 0's if unusable)
   uint32_t m;   // chooser byte of that cell; 0 if unusable
+  uint32_t kw;  // chooser bytes of the four cells whose keep masks this thread forms
 };
+
+// Thread ptid forms keep words 2q and 2q + 1 for position bit b = ptid & 7,
+// group q = (ptid >> 3) & 3, lane half hb = (ptid >> 5) & 1 and cell half
+// ch = ptid >> 6: they cover cells 4w..4w+3, w = 8ch + 2q + hb, whose chooser
+// bytes are word w of the ring's.
+__device__ __forceinline__ int keep_word(int ptid) {
+  return 8 * (ptid >> 6) + 2 * ((ptid >> 3) & 3) + ((ptid >> 5) & 1);
+}
 
 __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int ptid, Raw& r) {
 #pragma unroll
@@ -632,25 +640,40 @@ __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int
   const float* sp = (ptid < kChunk) ? a.k_scale : a.v_scale;
   r.sc = sp[rg.off[cell] / kD];   // zeroed at conversion, when the load has landed
   r.m = rg.mask[cell];
+  r.kw = reinterpret_cast<const uint32_t*>(rg.mask)[keep_word(ptid)];
 }
 
-__device__ __forceinline__ void convert(const PrefillArgs& a, const Stage& st, int ptid, const Raw& r,
-                                        uint32_t& flags) {
+// Keep masks from the chooser bytes of cells 4w..4w+3 (word w of the ring's
+// bytes) for position bit b: shifted so that bit b of bytes 0 and 2 lands on
+// bits 15 and 31 of lo, of bytes 1 and 3 on bits 15 and 31 of hi; byte
+// selectors 8..11 of v_perm replicate bits 15 and 31 of either source.
+__device__ __forceinline__ uint2 keep_words(uint32_t x, int b) {
+  const uint32_t lo = x << (15 - b);
+  const uint32_t hi = x << (7 - b);
+  return uint2{__builtin_amdgcn_perm(lo, hi, 0x08080a0au), __builtin_amdgcn_perm(lo, hi, 0x09090b0bu)};
+}
+
+__device__ __forceinline__ void convert(const PrefillArgs& a, const Stage& st, int ptid, bool kwave,
+                                        const Raw& r, uint32_t& flags) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     store_k_task(st, ptid + 128 * k, r.k[k]);
     store_v_task(st, ptid + 128 * k, r.v[k]);
   }
-  // wave 6 stores the k factors and chooser bytes, wave 7 the v factors (and
-  // a spare copy of the chooser bytes), without a branch
-  const bool kwave = ptid < kChunk;
+  // wave 6 stores the k factors, wave 7 the v factors
   const int lane = ptid & 63;
   const float sc = r.m ? r.sc : 0.f;
-  const bool v_ok = fabsf(sc) < kVScaleLimit;
-  flags |= (!kwave && !v_ok) ? SEL_ATTN_STATUS_V_SCALE : 0u;
-  const float mult = kwave ? a.score_scale : (v_ok ? kVFold : 0.f);
-  (kwave ? st.kf : st.vf)[lane] = sc * mult;
-  reinterpret_cast<uint8_t*>(kwave ? st.emask : st.emask_spare)[lane] = (uint8_t)r.m;
+  if (kwave) {
+    st.kf[lane] = sc * a.score_scale;
+  } else {
+    const bool v_ok = fabsf(sc) < kVScaleLimit;
+    flags |= v_ok ? 0u : SEL_ATTN_STATUS_V_SCALE;
+    st.vf[lane] = (_Float16)(v_ok ? sc * kVFold : 0.f);
+  }
+  // keep words 2q and 2q + 1 (q = (ptid >> 3) & 3) of position bit ptid & 7
+  const int q = (ptid >> 3) & 3;
+  uint32_t* kp = st.keep + 4 * keep_unit(ptid & 7, ptid >> 6, (ptid >> 5) & 1, q >> 1) + 2 * (q & 1);
+  *reinterpret_cast<uint2*>(kp) = keep_words(r.kw, ptid & 7);
 }
 
 // Producer state, each array indexed by chunk & 3: gathered rows (chunk x is
@@ -684,7 +707,7 @@ __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, Pro
   finish_translation(a, ps.pg[(P + kAheadFinish) & 3], U, cf, h,
                      sm.ring[translator ? (cf & (kRing - 1)) : kRing], lane, flags);
   gather(a, sm.ring[(c + kAheadGather) & (kRing - 1)], ptid, ps.raw[(P + kAheadGather) & 3]);
-  convert(a, stage(sm, P + 2), ptid, ps.raw[(P + 2) & 3], flags);
+  convert(a, stage(sm, P + 2), ptid, translator, ps.raw[(P + 2) & 3], flags);
   lds_barrier();
 }
 
@@ -718,12 +741,12 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
   lds_barrier();
 #pragma unroll
   for (int x = 0; x < kAheadGather; ++x) {
-    if (x >= 4) convert(a, stage(sm, x - 4), ptid, ps.raw[x & 3], flags);   // frees the set
+    if (x >= 4) convert(a, stage(sm, x - 4), ptid, translator, ps.raw[x & 3], flags);   // frees the set
     gather(a, sm.ring[x], ptid, ps.raw[x & 3]);
   }
 #pragma unroll
   for (int x = (kAheadGather > 4 ? kAheadGather - 4 : 0); x < 2; ++x)
-    convert(a, stage(sm, x), ptid, ps.raw[x & 3], flags);
+    convert(a, stage(sm, x), ptid, translator, ps.raw[x & 3], flags);
   lds_barrier();
   lds_barrier();   // the consumers have read chunk 0's K tile
 
