@@ -190,26 +190,19 @@ __device__ __forceinline__ uint32_t task_offset(const Ring& rg, int t) {
   return rg.off[task_cell(t)] + 16u * task_block(t);
 }
 
-// K is stored as exact FP16 integers (the offset removed with one packed FP16
-// subtraction per pair), so every S^T chain starts from zero.
-__device__ __forceinline__ uint32_t unbias_pair(uint32_t biased) {
-  const half2 h = __builtin_bit_cast(half2, biased) - half2{(_Float16)1152.f, (_Float16)1152.f};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
+// K keeps the offset too: Q.(k + 1152) = Q.k + 1152 sum(Q), and every S^T
+// chain starts from -1152 sum(Q) of its row instead of zero.
 __device__ __forceinline__ void store_k_task(const Stage& st, int t, u32x4 raw) {
   const int cell = task_cell(t);
   const int u0 = 2 * task_block(t);
   const uint2 b0 = i8x4_to_biased_half(raw.x), b1 = i8x4_to_biased_half(raw.y);
   const uint2 b2 = i8x4_to_biased_half(raw.z), b3 = i8x4_to_biased_half(raw.w);
-  const u32x4 a0 = u32x4{unbias_pair(b0.x), unbias_pair(b0.y), unbias_pair(b1.x), unbias_pair(b1.y)};
-  const u32x4 a1 = u32x4{unbias_pair(b2.x), unbias_pair(b2.y), unbias_pair(b3.x), unbias_pair(b3.y)};
   _Float16* base = st.k + cell * kKRow + 8 * u0;
-  *reinterpret_cast<u32x4*>(base) = a0;
-  *reinterpret_cast<u32x4*>(base + 8) = a1;
+  *reinterpret_cast<u32x4*>(base) = u32x4{b0.x, b0.y, b1.x, b1.y};
+  *reinterpret_cast<u32x4*>(base + 8) = u32x4{b2.x, b2.y, b3.x, b3.y};
 }
 
-// The V tile keeps v + 1152 too: the consumers track the sum of the FP16
+// The V tile keeps v + 1152: the consumers track the sum of the FP16
 // probabilities they multiply with it and remove 1152 times that sum at the end.
 __device__ __forceinline__ void store_v_task(const Stage& st, int t, u32x4 raw) {
   const int cell = task_cell(t);
@@ -283,11 +276,9 @@ __device__ __forceinline__ void finish_translation(const PrefillArgs& a, const P
 // Consumer waves 0..5: row block rb = w % 3 (32 rows), cell half ch = w / 3.
 // S^T (this wave's 32 cells x 32 rows) of one chunk. qrow: this lane's row of
 // the Q tile, at dims 8hb (k-step ks reads dims 16ks + 8hb .. +7).
-__device__ __forceinline__ float16v scores_t(const Stage& st, const _Float16* qrow, int ch, int hb,
-                                             int l32) {
-  float16v s;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+__device__ __forceinline__ float16v scores_t(const Stage& st, const _Float16* qrow,
+                                             const float16v& s_init, int ch, int hb, int l32) {
+  float16v s = s_init;
   const int cell = 32 * ch + l32;
   const _Float16* krow = st.k + cell * kKRow + 8 * hb;
 #pragma unroll
@@ -325,6 +316,7 @@ __device__ __forceinline__ half8 load_v_operand(const Stage& st, int ch, int ks,
 struct ConsState {
   float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^9
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
+  float16v s_init;    // -1152 sum(Q) of this lane's row, where every S^T chain starts
   half8 pb[2];        // P'^T of the previous chunk
   half8 vfrag[8];     // V^T operands of the previous chunk
   float m_run;        // running maximum (log2 domain) of this lane's row
@@ -340,6 +332,22 @@ struct ChunkFactors {
   half2 vf[8];
   uint32_t keep[8];
 };
+
+// Keep masks, v factors and the first two k-factor groups of chunk c.
+__device__ __forceinline__ void load_factors(ChunkFactors& f, const Stage& st, int ch, int hb, int l32) {
+  const u32x4* kp = reinterpret_cast<const u32x4*>(st.keep);
+  const u32x4 a0 = kp[keep_unit(l32 & 7, ch, hb, 0)], a1 = kp[keep_unit(l32 & 7, ch, hb, 1)];
+  f.keep[0] = a0.x; f.keep[1] = a0.y; f.keep[2] = a0.z; f.keep[3] = a0.w;
+  f.keep[4] = a1.x; f.keep[5] = a1.y; f.keep[6] = a1.z; f.keep[7] = a1.w;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const half4 v = *reinterpret_cast<const half4*>(st.vf + 32 * ch + 8 * q + 4 * hb);
+    f.vf[2 * q] = half2{v[0], v[1]};
+    f.vf[2 * q + 1] = half2{v[2], v[3]};
+  }
+  f.k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
+  f.k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
+}
 
 // Probability pair j (scores 2j, 2j+1) of chunk c: FP16, masked, summed into
 // psum; times the v factors into P'^T, summed into lpc.
@@ -363,13 +371,11 @@ __device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, co
                                               const _Float16* qrow, ChunkFactors& f,
                                               half8 kfrag[8], half8 qfrag[8], float16v& s_next,
                                               float& psum, float& lpc, int ch, int hb) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
   psum = 0.f;
   lpc = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qfrag[j], s_next, 0, 0, 0);
+    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qfrag[j], j == 0 ? cs.s_init : s_next, 0, 0, 0);
     if (j + 2 < 8) {
       kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
       qfrag[j + 2] = *reinterpret_cast<const half8*>(qrow + 16 * (j + 2));
@@ -401,20 +407,7 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   // LDS reads: chunk c's keep masks and v factors of this lane's cell pairs,
   // the first k factors
   ChunkFactors f;
-  {
-    const u32x4* kp = reinterpret_cast<const u32x4*>(st.keep);
-    const u32x4 a0 = kp[keep_unit(l32 & 7, ch, hb, 0)], a1 = kp[keep_unit(l32 & 7, ch, hb, 1)];
-    f.keep[0] = a0.x; f.keep[1] = a0.y; f.keep[2] = a0.z; f.keep[3] = a0.w;
-    f.keep[4] = a1.x; f.keep[5] = a1.y; f.keep[6] = a1.z; f.keep[7] = a1.w;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const half4 v = *reinterpret_cast<const half4*>(st.vf + 32 * ch + 8 * q + 4 * hb);
-      f.vf[2 * q] = half2{v[0], v[1]};
-      f.vf[2 * q + 1] = half2{v[2], v[3]};
-    }
-  }
-  f.k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
-  f.k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
+  load_factors(f, st, ch, hb, l32);
 
   // O^T += V^T P'^T of chunk c-1
 #pragma unroll
@@ -440,11 +433,17 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   // running maximum moved (what is accumulated is rescaled; this waits for the
   // MFMAs issued above) and the chunk redone against it
   if (__ballot(!(psum <= kLazyLimit))) {
+    // the chunk's factors again from LDS (registers are not held for this rare path)
+    ChunkFactors g;
+    load_factors(g, st, ch, hb, l32);
+#pragma unroll
+    for (int q4 = 2; q4 < 4; ++q4)
+      g.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
     float cmax = ninf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const bool keep = (f.keep[r >> 1] >> (16 * (r & 1))) & 1u;
-      cmax = fmaxf(cmax, keep ? cs.s_cur[r] * f.k4[r >> 2][r & 3] : ninf);
+      const bool keep = (g.keep[r >> 1] >> (16 * (r & 1))) & 1u;
+      cmax = fmaxf(cmax, keep ? cs.s_cur[r] * g.k4[r >> 2][r & 3] : ninf);
     }
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
     const float m_new = fmaxf(cs.m_run, cmax);
@@ -461,8 +460,8 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = 2 * j;
-      prob_pair(cs, f, j, __builtin_fmaf(cs.s_cur[r], f.k4[r >> 2][r & 3], -cs.m_run),
-                __builtin_fmaf(cs.s_cur[r + 1], f.k4[r >> 2][(r + 1) & 3], -cs.m_run), psum, lpc);
+      prob_pair(cs, g, j, __builtin_fmaf(cs.s_cur[r], g.k4[r >> 2][r & 3], -cs.m_run),
+                __builtin_fmaf(cs.s_cur[r + 1], g.k4[r >> 2][(r + 1) & 3], -cs.m_run), psum, lpc);
     }
   }
   cs.l_run += psum;
@@ -541,7 +540,21 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) cs.pb[ks][e] = (_Float16)0.f;
-  cs.s_cur = scores_t(stage(sm, 0), qrow, ch, hb, l32);
+  {
+    // -1152 times the sum of this lane's row of FP16 Q (both lane halves' dims)
+    const half2 one = {(_Float16)1.f, (_Float16)1.f};
+    float qs = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const half8 x = *reinterpret_cast<const half8*>(qrow + 16 * s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qs = __builtin_amdgcn_fdot2(half2{x[2 * e], x[2 * e + 1]}, one, qs, false);
+    }
+    const float init = -1152.f * (qs + __shfl_xor(qs, 32));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cs.s_init[r] = init;
+  }
+  cs.s_cur = scores_t(stage(sm, 0), qrow, cs.s_init, ch, hb, l32);
   lds_barrier();   // prologue: chunk 0's K tile read (the producers rewrite it next)
 
   consume_chunks(cs, sm, qrow, ch, hb, l32, nch);
