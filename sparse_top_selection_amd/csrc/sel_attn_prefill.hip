@@ -32,19 +32,21 @@
 //   * each consumer iteration issues the O^T update of chunk c-1, then the
 //     S^T(c+1) chain with the softmax of chunk c between its MFMAs, so the
 //     matrix pipe and the VALU work at the same time;
-//   * K and V integers are exact in FP16, so the scales are applied in FP32:
-//     k_scale * softmax_scale * log2(e) multiplies the score, v_scale * 2^10 the
-//     probability before its FP16 rounding (2^-10 returns in the epilogue). The
-//     V tile keeps the +1152 offset of the byte-to-FP16 trick; each lane tracks
-//     the sum of the FP16 probabilities it feeds the MFMA and 1152 times that
-//     sum is removed once at the end;
-//   * a lane's 16 keep flags come from its cells' chooser bytes: one AND with
-//     the lane's bit in every byte, one byte-select compare per score; one
-//     v_cndmask applies each;
+//   * K and V integers (plus the +1152 offset of the byte-to-FP16 trick) are
+//     exact in FP16; the K offset is removed by starting each S^T chain from
+//     -1152 sum(Q) of its row, k_scale * softmax_scale * log2(e) multiplies
+//     the score in FP32, and the FP16 probabilities are multiplied by the FP16
+//     v factor v_scale * 2^6 (2^-6 returns in the epilogue). Each lane tracks
+//     the sum of the P' values it feeds the MFMA; 1152 times that sum (the V
+//     offset) is removed once at the end;
+//   * keep masks: the producers expand the chooser bytes into 16-bit all-ones
+//     or zero masks per (position bit, cell), laid out so that a consumer lane
+//     reads the eight words of its cell pairs with two 16-byte loads and
+//     applies them with one AND per pair of packed FP16 probabilities;
 //   * online softmax with a lazy stabiliser: probabilities are taken against
-//     the running maximum, and only when a lane's chunk sum exceeds 16 does the
-//     wave recompute the chunk maximum and rescale O, l and the probability sum
-//     (always on a row's first chosen chunk, rarely after).
+//     the running maximum (set from chunk 0's scores), and only when a lane's
+//     chunk sum exceeds 128 does the wave recompute the chunk maximum and
+//     rescale O, l and the P' sum.
 
 #include "sel_attn_internal.h"
 
@@ -70,10 +72,10 @@ constexpr int kRows = 8 * kQPerKv;  // rows of a work-group: 8 positions x 12 qu
 constexpr int kKRow = kD + 8;       // K and Q tile rows: 128 dims + 16 bytes of padding
 constexpr int kLead = 3;            // iterations between a read and its first use (producers)
 constexpr int kRing = 8;            // translated chunks (ring slots, indexed by chunk & 7)
-constexpr float kLazyLimit = 16.f;
+constexpr float kLazyLimit = 128.f;  // a lane's chunk probability sum, against the running maximum
 constexpr float kNoMax = -1e30f;    // stabiliser before a row has seen a chosen cell
-constexpr float kVFold = 512.f;     // the FP16 v factor is v_scale * 2^9
-constexpr float kVScaleLimit = 4.f; // so that v factor (< 2^11) times probability (<= 16) fits FP16
+constexpr float kVFold = 64.f;      // the FP16 v factor is v_scale * 2^6
+constexpr float kVScaleLimit = 4.f; // so that v factor (<= 2^8) times probability (<= 2^7) fits FP16
 
 // LDS: the four stages' K tiles, then their V tiles, so that a stage's tile
 // addresses differ by multiples of the tile size that fit the 16-bit immediate
@@ -314,7 +316,7 @@ __device__ __forceinline__ half8 load_v_operand(const Stage& st, int ch, int ks,
 
 // Registers a consumer wave carries from one iteration to the next.
 struct ConsState {
-  float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^9
+  float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^6
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
   float16v s_init;    // -1152 sum(Q) of this lane's row, where every S^T chain starts
   half8 pb[2];        // P'^T of the previous chunk
@@ -429,7 +431,7 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   float psum, lpc;
   chain_softmax(cs, st, krow, qrow, f, kfrag, qfrag, s_next, psum, lpc, ch, hb);
 
-  // the lazy stabiliser: only when some lane's chunk sum leaves [0, 16] is the
+  // the lazy stabiliser: only when some lane's chunk sum leaves [0, 128] is the
   // running maximum moved (what is accumulated is rescaled; this waits for the
   // MFMAs issued above) and the chunk redone against it
   if (__ballot(!(psum <= kLazyLimit))) {
@@ -555,6 +557,23 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
     for (int r = 0; r < 16; ++r) cs.s_init[r] = init;
   }
   cs.s_cur = scores_t(stage(sm, 0), qrow, cs.s_init, ch, hb, l32);
+  {
+    // the running maximum starts at chunk 0's maximum over this row's chosen
+    // cells, so that the first chunk needs no rescale (the sinks lead the union)
+    const Stage st = stage(sm, 0);
+    ChunkFactors g;
+    load_factors(g, st, ch, hb, l32);
+#pragma unroll
+    for (int q4 = 2; q4 < 4; ++q4)
+      g.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+    float cmax = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool keep = (g.keep[r >> 1] >> (16 * (r & 1))) & 1u;
+      cmax = fmaxf(cmax, keep ? cs.s_cur[r] * g.k4[r >> 2][r & 3] : -__builtin_inff());
+    }
+    cs.m_run = fmaxf(kNoMax, fmaxf(cmax, __shfl_xor(cmax, 32)));
+  }
   lds_barrier();   // prologue: chunk 0's K tile read (the producers rewrite it next)
 
   consume_chunks(cs, sm, qrow, ch, hb, l32, nch);
