@@ -138,7 +138,8 @@ int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32
  *   status       uint32 [1]                             in/out, as above
  *   Precision: Q, dequantised K, V and the probabilities enter the products as
  *   FP16 (round to nearest even); scores, softmax and sums are FP32. K and V
- *   integers are exact in FP16; their scales are applied in FP32.
+ *   integers are exact in FP16; k_scale is applied to the FP32 score, v_scale
+ *   as an FP16 factor (v_scale * 2^6) on the FP16 probability.
  *   Supported scales: |v_scale| < 4 (other values set V_SCALE); k_scale any
  *   finite value.
  *   Errors: CELL_RANGE, PAGE_RANGE, UNION_LEN, V_SCALE as listed above; a bad
