@@ -2,7 +2,8 @@
 // FP32 online softmax with a per-position chooser mask.
 //
 // Page: #2808 "sycl: prompt attention over 8-query selection unions on XMX".
-//   section Summary: 64-cell chunks of the union are dequantised once to FP16;
+//   section Summary: chunks of the union are dequantised once to FP16 (the
+//     page's chunks hold 64 cells, these 32);
 //     S^T = K Q^T and O += P V run on matrix units with FP32 sums for all 96 rows
 //     (8 positions x 12 heads); in the online softmax a cell is -inf for the
 //     positions that did not choose it; Q, K, V and P enter the products as FP16.
@@ -11,19 +12,19 @@
 //
 // gfx950 mapping (the page's 16-lane sub-group / 256-GRF shape is Xe2 prior art
 // and is not reproduced):
-//   * one 512-thread workgroup (8 wave64s, one per CU at this register budget,
-//     two per SIMD) per (group g, KV head h); grid order is XCD-aware so that
-//     each XCD walks consecutive groups of one KV head;
-//   * waves 0..5 consume, waves 6..7 produce (at raised priority: every wave
-//     waits for their stage at the barrier). The producers translate union
-//     cells through the page table and gather the INT8 K/V rows with 16-byte
-//     loads, every read consumed kLead iterations after it was issued, convert
-//     the rows to FP16 and store them into LDS (K tiles in two stages, V tiles
-//     and per-cell factors in four); the consumers only read LDS;
+//   * one 256-thread workgroup (4 wave64s, under 80 KB of LDS, so that two
+//     share a CU and one's prologue and epilogue overlap the other's chunk
+//     loop) per (group g, KV head h); grid order is XCD-aware so that each XCD
+//     walks consecutive groups of one KV head;
+//   * waves 0..2 consume, wave 3 produces (at raised priority: every wave waits
+//     for its stage at the barrier). The producer translates union cells
+//     through the page table and gathers the INT8 K/V rows with 16-byte loads,
+//     every read consumed kLead iterations after it was issued, converts the
+//     rows to FP16 and stores them into LDS (K tiles in two stages, V tiles and
+//     per-cell factors in four); the consumers only read LDS;
 //   * row n of the 96 = 8*hq + i (query head h*12+hq, position 8g+i), so the
-//     chooser bit of row n is n & 7; consumer wave w owns row block rb = w % 3
-//     (32 rows) and cell half ch = w / 3 (32 of each chunk's 64 cells) with its
-//     own softmax state; the two halves are merged once at the end;
+//     chooser bit of row n is n & 7; consumer wave w owns row block w (32 rows)
+//     and every cell of each chunk, with its own softmax state;
 //   * S^T (32 cells x 32 rows, K=128) is 8 v_mfma_f32_32x32x16_f16 from the K
 //     tile and the work-group's Q tile (both in LDS); O^T (128 dims x 32 rows)
 //     += V^T P'^T is 8 more MFMAs whose B operand (P'^T) comes straight from
@@ -60,10 +61,10 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kConsumerWaves = 6;   // 3 row blocks x 2 cell halves
-constexpr int kProducerWaves = 2;   // translate, gather, convert
+constexpr int kConsumerWaves = 3;   // one per row block of 32
+constexpr int kProducerWaves = 1;   // translate, gather, convert
 constexpr int kThreads = 64 * (kConsumerWaves + kProducerWaves);
-constexpr int kChunk = 64;          // union cells per iteration
+constexpr int kChunk = 32;          // union cells per iteration
 constexpr int kD = 128;             // head dim
 constexpr int kQPerKv = 12;
 constexpr int kStages = 4;          // V tiles and factors: chunks c (read), c+1, c+2 (written)
@@ -93,8 +94,11 @@ struct __align__(16) Smem {
   _Float16 vf[kStages][kChunk];         // FP16(v_scale * 2^9); 0 where unusable
   uint32_t keep[kStages][4 * kChunk];   // keep masks, 16-byte units laid out by keep_unit()
   _Float16 q[kRows * kKRow];            // the work-group's Q, [row][dim] in FP16, rows of kKRow
-  Ring ring[kRing + 1];   // the last slot takes the second producer wave's copies
+  Ring ring[kRing + 1];   // the last slot takes the upper producer lanes' copies
 };
+// two work-groups share a CU (LDS 160 KB): one's prologue and epilogue overlap
+// the other's chunk loop
+static_assert(sizeof(Smem) <= 80 * 1024, "two work-groups per CU");
 
 // The parts of the stages that hold chunk c.
 struct Stage {
@@ -110,16 +114,13 @@ __device__ __forceinline__ Stage stage(Smem& sm, int c) {
   return Stage{sm.k[c & (kKStages - 1)], sm.v[s], sm.kf[s], sm.vf[s], sm.keep[s]};
 }
 
-// Keep masks of a chunk: for position bit b (row & 7), cell half ch and lane
-// half hb, eight words; word 2q + j holds in its low and high 16 bits all-ones
-// or zero for cells 32ch + 8q + 4hb + 2j and +1 (the cells, in order, whose
-// scores a consumer lane packs into its j-th probability pair of group q).
-// Words 4u..4u+3 form 16-byte unit keep_unit(b, ch, hb, u): the eight position
-// bits of a unit are adjacent, so the eight rows of a lane octet read eight
-// distinct bank groups.
-__device__ __forceinline__ int keep_unit(int b, int ch, int hb, int u) {
-  return ((2 * ch + hb) * 2 + u) * 8 + b;
-}
+// Keep masks of a chunk: for position bit b (row & 7) and lane half hb, eight
+// words; word 2q + j holds in its low and high 16 bits all-ones or zero for
+// cells 8q + 4hb + 2j and +1 (the cells, in order, whose scores a consumer
+// lane packs into its j-th probability pair of group q). Words 4u..4u+3 form
+// 16-byte unit keep_unit(b, hb, u): the eight position bits of a unit are
+// adjacent, so the eight rows of a lane octet read eight distinct bank groups.
+__device__ __forceinline__ int keep_unit(int b, int hb, int u) { return (2 * hb + u) * 8 + b; }
 
 // ---------------------------------------------------------------------------
 // Workgroup barrier that orders LDS only. Threads of a workgroup talk to each
@@ -275,13 +276,13 @@ __device__ __forceinline__ void finish_translation(const PrefillArgs& a, const P
 }
 
 // ---------------------------------------------------------------------------
-// Consumer waves 0..5: row block rb = w % 3 (32 rows), cell half ch = w / 3.
-// S^T (this wave's 32 cells x 32 rows) of one chunk. qrow: this lane's row of
+// Consumer waves 0..2: row block w (32 rows).
+// S^T (the chunk's 32 cells x this wave's 32 rows). qrow: this lane's row of
 // the Q tile, at dims 8hb (k-step ks reads dims 16ks + 8hb .. +7).
 __device__ __forceinline__ float16v scores_t(const Stage& st, const _Float16* qrow,
-                                             const float16v& s_init, int ch, int hb, int l32) {
+                                             const float16v& s_init, int hb, int l32) {
   float16v s = s_init;
-  const int cell = 32 * ch + l32;
+  const int cell = l32;
   const _Float16* krow = st.k + cell * kKRow + 8 * hb;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -296,14 +297,14 @@ __device__ __forceinline__ float16v scores_t(const Stage& st, const _Float16* qr
 // transposed from the [cell][dim] V tile with ds_read_b64_tr_b16: within each
 // group of 16 lanes, lane i receives element i % 4 of the 8-byte rows addressed
 // by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4. Lane l addresses cell
-// 32ch + 16ks + 4hb + ((l & 15) >> 2) (and the same + 8 for the second half)
+// 16ks + 4hb + ((l & 15) >> 2) (and the same + 8 for the second half)
 // at dims 32mb + 16((l >> 4) & 1) + 4(l & 3), so it receives dim 32mb + (l & 31)
 // of the eight cells whose P'^T values it holds, in the same order.
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
-__device__ __forceinline__ half8 load_v_operand(const Stage& st, int ch, int ks, int mb, int lane) {
+__device__ __forceinline__ half8 load_v_operand(const Stage& st, int ks, int mb, int lane) {
   const int hb = lane >> 5;
-  const int c0 = 32 * ch + 16 * ks + 4 * hb + ((lane & 15) >> 2);
+  const int c0 = 16 * ks + 4 * hb + ((lane & 15) >> 2);
   const int dimb = 64 * mb + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);   // byte in the row
   const int pos = v_pos(dimb >> 4, c0);   // the same for cell c0 + 8
   const char* row0 = reinterpret_cast<const char*>(st.v) + c0 * (kD * 2) + (pos << 4) + (dimb & 15);
@@ -336,19 +337,19 @@ struct ChunkFactors {
 };
 
 // Keep masks, v factors and the first two k-factor groups of chunk c.
-__device__ __forceinline__ void load_factors(ChunkFactors& f, const Stage& st, int ch, int hb, int l32) {
+__device__ __forceinline__ void load_factors(ChunkFactors& f, const Stage& st, int hb, int l32) {
   const u32x4* kp = reinterpret_cast<const u32x4*>(st.keep);
-  const u32x4 a0 = kp[keep_unit(l32 & 7, ch, hb, 0)], a1 = kp[keep_unit(l32 & 7, ch, hb, 1)];
+  const u32x4 a0 = kp[keep_unit(l32 & 7, hb, 0)], a1 = kp[keep_unit(l32 & 7, hb, 1)];
   f.keep[0] = a0.x; f.keep[1] = a0.y; f.keep[2] = a0.z; f.keep[3] = a0.w;
   f.keep[4] = a1.x; f.keep[5] = a1.y; f.keep[6] = a1.z; f.keep[7] = a1.w;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const half4 v = *reinterpret_cast<const half4*>(st.vf + 32 * ch + 8 * q + 4 * hb);
+    const half4 v = *reinterpret_cast<const half4*>(st.vf + 8 * q + 4 * hb);
     f.vf[2 * q] = half2{v[0], v[1]};
     f.vf[2 * q + 1] = half2{v[2], v[3]};
   }
-  f.k4[0] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 4 * hb);
-  f.k4[1] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 + 4 * hb);
+  f.k4[0] = *reinterpret_cast<const float4v*>(st.kf + 4 * hb);
+  f.k4[1] = *reinterpret_cast<const float4v*>(st.kf + 8 + 4 * hb);
 }
 
 // Probability pair j (scores 2j, 2j+1) of chunk c: FP16, masked, summed into
@@ -372,7 +373,7 @@ __device__ __forceinline__ void prob_pair(ConsState& cs, const ChunkFactors& f, 
 __device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, const _Float16* krow,
                                               const _Float16* qrow, ChunkFactors& f,
                                               half8 kfrag[8], half8 qfrag[8], float16v& s_next,
-                                              float& psum, float& lpc, int ch, int hb) {
+                                              float& psum, float& lpc, int hb) {
   psum = 0.f;
   lpc = 0.f;
 #pragma unroll
@@ -387,7 +388,7 @@ __device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, co
               __builtin_fmaf(cs.s_cur[r + 1], f.k4[r >> 2][(r + 1) & 3], -cs.m_run), psum, lpc);
     if (j == 1 || j == 3) {   // k factors two MFMAs ahead of their scores
       const int q4 = (j + 3) >> 1;
-      f.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+      f.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 8 * q4 + 4 * hb);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -401,7 +402,7 @@ __device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, co
 // (their LDS latency passes during the barrier).
 template <int P>
 __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Float16* qrow,
-                                             int ch, int hb, int l32) {
+                                             int hb, int l32) {
   const Stage st = stage(sm, P);            // chunk c: factors, keep masks, V
   const Stage st_next = stage(sm, P + 1);   // chunk c+1: K
   const float ninf = -__builtin_inff();
@@ -409,7 +410,7 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   // LDS reads: chunk c's keep masks and v factors of this lane's cell pairs,
   // the first k factors
   ChunkFactors f;
-  load_factors(f, st, ch, hb, l32);
+  load_factors(f, st, hb, l32);
 
   // O^T += V^T P'^T of chunk c-1
 #pragma unroll
@@ -419,8 +420,7 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   // the first two of chunk c+1's K operands and Q's (the others are read two
   // MFMAs ahead of their use in the chain below)
   half8 kfrag[8], qfrag[8];
-  const int cell = 32 * ch + l32;
-  const _Float16* krow = st_next.k + cell * kKRow + 8 * hb;
+  const _Float16* krow = st_next.k + l32 * kKRow + 8 * hb;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     kfrag[j] = *reinterpret_cast<const half8*>(krow + 16 * j);
@@ -429,7 +429,7 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
 
   float16v s_next;
   float psum, lpc;
-  chain_softmax(cs, st, krow, qrow, f, kfrag, qfrag, s_next, psum, lpc, ch, hb);
+  chain_softmax(cs, st, krow, qrow, f, kfrag, qfrag, s_next, psum, lpc, hb);
 
   // the lazy stabiliser: only when some lane's chunk sum leaves [0, 128] is the
   // running maximum moved (what is accumulated is rescaled; this waits for the
@@ -437,10 +437,10 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   if (__ballot(!(psum <= kLazyLimit))) {
     // the chunk's factors again from LDS (registers are not held for this rare path)
     ChunkFactors g;
-    load_factors(g, st, ch, hb, l32);
+    load_factors(g, st, hb, l32);
 #pragma unroll
     for (int q4 = 2; q4 < 4; ++q4)
-      g.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+      g.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 8 * q4 + 4 * hb);
     float cmax = ninf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -472,30 +472,29 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   // chunk c's V^T operands for the next iteration's update (stage c & 3 is
   // rewritten only three iterations from now)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) cs.vfrag[j] = load_v_operand(st, ch, j >> 2, j & 3, (hb << 5) | l32);
+  for (int j = 0; j < 8; ++j) cs.vfrag[j] = load_v_operand(st, j >> 2, j & 3, (hb << 5) | l32);
   cs.s_cur = s_next;
   consumer_barrier();
 }
 
 __device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, const _Float16* qrow,
-                                               int ch, int hb, int l32, int nch) {
+                                               int hb, int l32, int nch) {
   int c = 0;
   for (; c + 4 <= nch; c += 4) {
-    consume_step<0>(cs, sm, qrow, ch, hb, l32);
-    consume_step<1>(cs, sm, qrow, ch, hb, l32);
-    consume_step<2>(cs, sm, qrow, ch, hb, l32);
-    consume_step<3>(cs, sm, qrow, ch, hb, l32);
+    consume_step<0>(cs, sm, qrow, hb, l32);
+    consume_step<1>(cs, sm, qrow, hb, l32);
+    consume_step<2>(cs, sm, qrow, hb, l32);
+    consume_step<3>(cs, sm, qrow, hb, l32);
   }
   const int rem = nch - c;
-  if (rem > 0) consume_step<0>(cs, sm, qrow, ch, hb, l32);
-  if (rem > 1) consume_step<1>(cs, sm, qrow, ch, hb, l32);
-  if (rem > 2) consume_step<2>(cs, sm, qrow, ch, hb, l32);
+  if (rem > 0) consume_step<0>(cs, sm, qrow, hb, l32);
+  if (rem > 1) consume_step<1>(cs, sm, qrow, hb, l32);
+  if (rem > 2) consume_step<2>(cs, sm, qrow, hb, l32);
 }
 
 __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
                                         int nch, int wave, int lane) {
-  const int rb = wave % 3;
-  const int ch = wave / 3;
+  const int rb = wave;
   const int hb = lane >> 5;
   const int l32 = lane & 31;
   const int n_qh = a.n_kv * kQPerKv;
@@ -507,10 +506,9 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   const bool row_ok = qi < a.n_q;
 
   // Q in FP16 into the Q tile (the B operand of S^T = K Q^T is read from there:
-  // k-step s covers dims 16s..16s+15, lane half hb dims 16s + 8hb .. +7); the
-  // ch = 0 wave of each row block stores its rows.
+  // k-step s covers dims 16s..16s+15, lane half hb dims 16s + 8hb .. +7)
   _Float16* qrow = sm.q + row_n * kKRow + 8 * hb;
-  if (ch == 0) {
+  {
     const float* qg = a.q + ((int64_t)(row_ok ? qi : 0) * n_qh + h * kQPerKv + hq) * kD;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -556,16 +554,16 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 #pragma unroll
     for (int r = 0; r < 16; ++r) cs.s_init[r] = init;
   }
-  cs.s_cur = scores_t(stage(sm, 0), qrow, cs.s_init, ch, hb, l32);
+  cs.s_cur = scores_t(stage(sm, 0), qrow, cs.s_init, hb, l32);
   {
     // the running maximum starts at chunk 0's maximum over this row's chosen
     // cells, so that the first chunk needs no rescale (the sinks lead the union)
     const Stage st = stage(sm, 0);
     ChunkFactors g;
-    load_factors(g, st, ch, hb, l32);
+    load_factors(g, st, hb, l32);
 #pragma unroll
     for (int q4 = 2; q4 < 4; ++q4)
-      g.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 32 * ch + 8 * q4 + 4 * hb);
+      g.k4[q4] = *reinterpret_cast<const float4v*>(st.kf + 8 * q4 + 4 * hb);
     float cmax = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -576,99 +574,61 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   }
   lds_barrier();   // prologue: chunk 0's K tile read (the producers rewrite it next)
 
-  consume_chunks(cs, sm, qrow, ch, hb, l32, nch);
+  consume_chunks(cs, sm, qrow, hb, l32, nch);
   // the last chunk's O^T update
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[j], cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
-  // remove the V tile's offset: 1152 times the row's sum of P'^T values
-  {
-    const float corr = 1152.f * (cs.lp + __shfl_xor(cs.lp, 32));
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cs.o[mb][r] -= corr;
-  }
-  const float m_run = cs.m_run;
-  const float l_run = cs.l_run;
-  float16v* o = cs.o;
-  lds_barrier();   // every wave is done with the tiles the merge reuses
 
-  // ---- merge the two cell halves of each row block and write the output
-  float* xo = reinterpret_cast<float*>(&sm.v[0][0]);   // [3][16 float4 groups][64 lanes][4]
-  float* xm = xo + 3 * 64 * 64;                      // [3][64]
-  float* xl = xm + 3 * 64;                           // [3][64]
-  if (ch == 1) {
+  // out = (O^T - 1152 sum(P'), the V tile's offset) * 2^-6 / l; the row's sums
+  // are split over the two lane halves (their cells)
+  const float corr = 1152.f * (cs.lp + __shfl_xor(cs.lp, 32));
+  const float lt = cs.l_run + __shfl_xor(cs.l_run, 32);
+  const float inv = lt > 0.f ? (1.f / kVFold) / lt : 0.f;
+  if (row_ok) {
+    float* orow = a.out + ((int64_t)qi * n_qh + h * kQPerKv + hq) * kD;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4v v = {o[mb][4 * q4], o[mb][4 * q4 + 1], o[mb][4 * q4 + 2], o[mb][4 * q4 + 3]};
-        *reinterpret_cast<float4v*>(xo + ((rb * 16 + mb * 4 + q4) * 64 + lane) * 4) = v;
+        float4v r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (cs.o[mb][4 * q4 + e] - corr) * inv;
+        *reinterpret_cast<float4v*>(orow + 32 * mb + 8 * q4 + 4 * hb) = r;
       }
-    xm[rb * 64 + lane] = m_run;
-    xl[rb * 64 + lane] = l_run;
-  }
-  lds_barrier();
-  if (ch == 0) {
-    const float m1 = xm[rb * 64 + lane];
-    const float l1 = xl[rb * 64 + lane] + xl[rb * 64 + (lane ^ 32)];
-    const float l0 = l_run + __shfl_xor(l_run, 32);
-    const float mm = fmaxf(m_run, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m_run - mm);
-    const float a1 = __builtin_amdgcn_exp2f(m1 - mm);
-    const float lt = a0 * l0 + a1 * l1;
-    const float inv = lt > 0.f ? (1.f / kVFold) / lt : 0.f;
-    if (row_ok) {
-      float* orow = a.out + ((int64_t)qi * n_qh + h * kQPerKv + hq) * kD;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4v o1 =
-              *reinterpret_cast<const float4v*>(xo + ((rb * 16 + mb * 4 + q4) * 64 + lane) * 4);
-          float4v r;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = (a0 * o[mb][4 * q4 + e] + a1 * o1[e]) * inv;
-          *reinterpret_cast<float4v*>(orow + 32 * mb + 8 * q4 + 4 * hb) = r;
-        }
-    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Producer waves 6..7 (128 threads, ptid = tid - 384). Iteration c (while the
+// Producer wave 3 (64 threads, ptid = tid - 192). Iteration c (while the
 // consumers work on chunks c and c+1): read the union entries of chunk
 // c+kAheadUnion, the page-table entries of chunk c+kAheadPage, publish the
 // pool rows of chunk c+kAheadFinish in the ring, gather chunk c+kAheadGather
 // into registers and convert chunk c+2 (gathered kLead iterations earlier) into
-// its LDS stages. Each thread owns tasks ptid + 128k (k = 0..3) of both pools,
-// and the k scale (ptid < 64) or v scale of cell ptid & 63; both waves
-// translate the same lanes, wave 6 into the ring.
+// its LDS stages. Each thread owns tasks ptid + 64k (k = 0..3) of both pools,
+// and the k scale (ptid < 32) or v scale of cell ptid & 31; both lane halves
+// translate cell ptid & 31, the lower half into the ring.
 struct Raw {
   u32x4 k[4];
   u32x4 v[4];
-  float sc;     // k scale (wave 6) or v scale (wave 7) of cell ptid & 63 (row 0's if unusable)
+  float sc;     // k scale (ptid < 32) or v scale of cell ptid & 31 (row 0's if unusable)
   uint32_t m;   // chooser byte of that cell; 0 if unusable
   uint32_t kw;  // chooser bytes of the four cells whose keep masks this thread forms
 };
 
 // Thread ptid forms keep words 2q and 2q + 1 for position bit b = ptid & 7,
-// group q = (ptid >> 3) & 3, lane half hb = (ptid >> 5) & 1 and cell half
-// ch = ptid >> 6: they cover cells 4w..4w+3, w = 8ch + 2q + hb, whose chooser
-// bytes are word w of the ring's.
-__device__ __forceinline__ int keep_word(int ptid) {
-  return 8 * (ptid >> 6) + 2 * ((ptid >> 3) & 3) + ((ptid >> 5) & 1);
-}
+// group q = (ptid >> 3) & 3 and lane half hb = ptid >> 5: they cover cells
+// 4w..4w+3, w = 2q + hb, whose chooser bytes are word w of the ring's.
+__device__ __forceinline__ int keep_word(int ptid) { return 2 * ((ptid >> 3) & 3) + (ptid >> 5); }
 
 __device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int ptid, Raw& r) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t off = task_offset(rg, ptid + 128 * k);
+    const uint32_t off = task_offset(rg, ptid + 64 * k);
     r.k[k] = *reinterpret_cast<const u32x4*>(a.k_pool + off);
     r.v[k] = *reinterpret_cast<const u32x4*>(a.v_pool + off);
   }
-  const int cell = ptid & 63;
+  const int cell = ptid & (kChunk - 1);
   const float* sp = (ptid < kChunk) ? a.k_scale : a.v_scale;
   r.sc = sp[rg.off[cell] / kD];   // zeroed at conversion, when the load has landed
   r.m = rg.mask[cell];
@@ -689,11 +649,11 @@ __device__ __forceinline__ void convert(const PrefillArgs& a, const Stage& st, i
                                         const Raw& r, uint32_t& flags) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    store_k_task(st, ptid + 128 * k, r.k[k]);
-    store_v_task(st, ptid + 128 * k, r.v[k]);
+    store_k_task(st, ptid + 64 * k, r.k[k]);
+    store_v_task(st, ptid + 64 * k, r.v[k]);
   }
-  // wave 6 stores the k factors, wave 7 the v factors
-  const int lane = ptid & 63;
+  // the lower lane half stores the k factors, the upper the v factors
+  const int lane = ptid & (kChunk - 1);
   const float sc = r.m ? r.sc : 0.f;
   if (kwave) {
     st.kf[lane] = sc * a.score_scale;
@@ -704,7 +664,7 @@ __device__ __forceinline__ void convert(const PrefillArgs& a, const Stage& st, i
   }
   // keep words 2q and 2q + 1 (q = (ptid >> 3) & 3) of position bit ptid & 7
   const int q = (ptid >> 3) & 3;
-  uint32_t* kp = st.keep + 4 * keep_unit(ptid & 7, ptid >> 6, (ptid >> 5) & 1, q >> 1) + 2 * (q & 1);
+  uint32_t* kp = st.keep + 4 * keep_unit(ptid & 7, ptid >> 5, q >> 1) + 2 * (q & 1);
   *reinterpret_cast<uint2*>(kp) = keep_words(r.kw, ptid & 7);
 }
 
@@ -732,7 +692,7 @@ template <int P>
 __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, ProdState& ps, int c,
                                              int h, int U, int64_t ubase, int ptid, bool translator,
                                              uint32_t& flags) {
-  const int lane = ptid & 63;
+  const int lane = ptid & (kChunk - 1);
   ps.un[(P + kAheadUnion) & 3] = read_union_entry(a, ubase, U, c + kAheadUnion, lane);
   ps.pg[(P + kAheadPage) & 3] = read_page_entry(a, ps.un[(P + kAheadPage) & 3]);
   const int cf = c + kAheadFinish;
@@ -748,13 +708,13 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
                                         uint32_t& flags) {
   static_assert(kLead >= 1 && kLead <= 3 && kStages == 4 && kAheadFinish <= kRing,
                 "register sets and ring slots cover the lead");
-  const int lane = ptid & 63;
+  const int lane = ptid & (kChunk - 1);
   ProdState ps;
   // prologue: what iteration 0 expects. Chunks below kAheadFinish translated
   // into their ring slots; page records of the next kLead chunks and union
   // records of the kLead after those read; chunks 0 and 1 staged, chunks 2 ..
-  // kAheadGather-1 gathered. Both producer waves translate the same lanes;
-  // wave 7 writes its copy to the spare slot.
+  // kAheadGather-1 gathered. Both lane halves translate the same cells; the
+  // upper half writes its copy to the spare slot.
   {
     UnionRec u[kAheadPage];
 #pragma unroll
@@ -793,11 +753,9 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
   if (rem > 0) produce_step<0>(a, sm, ps, c, h, U, ubase, ptid, translator, flags);
   if (rem > 1) produce_step<1>(a, sm, ps, c + 1, h, U, ubase, ptid, translator, flags);
   if (rem > 2) produce_step<2>(a, sm, ps, c + 2, h, U, ubase, ptid, translator, flags);
-  lds_barrier();   // consumers finish their last O^T update
-  lds_barrier();   // merge of the consumers' two cell halves
 }
 
-__global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void sel_attn_prefill_kernel(PrefillArgs a) {
   __shared__ Smem sm;
 
   const int b = blockIdx.x;
@@ -818,7 +776,7 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
     flags |= SEL_ATTN_STATUS_UNION_LEN;
     U = U < 0 ? 0 : (int)ucap;
   }
-  const int nch = (U + kChunk - 1) / kChunk;   // 64-cell chunks of the union
+  const int nch = (U + kChunk - 1) / kChunk;   // chunks of the union
 
   if (wave < kConsumerWaves) {
     consume(a, sm, g, h, nch, wave, lane);
@@ -827,7 +785,7 @@ __global__ __launch_bounds__(kThreads) void sel_attn_prefill_kernel(PrefillArgs 
     // barrier), so their instructions go first on the SIMDs they share
     __builtin_amdgcn_s_setprio(1);
     const int ptid = tid - 64 * kConsumerWaves;
-    produce(a, sm, h, U, nch, ubase, ptid, wave == kConsumerWaves, flags);
+    produce(a, sm, h, U, nch, ubase, ptid, ptid < kChunk, flags);
   }
   if (flags) atomicOr(a.status, flags);
 }
