@@ -26,7 +26,8 @@
 //     chooser bit of row n is n & 7; consumer wave w owns row block w (32 rows)
 //     and every cell of each chunk, with its own softmax state;
 //   * S^T (32 cells x 32 rows, K=128) is 8 v_mfma_f32_32x32x16_f16 from the K
-//     tile and the work-group's Q tile (both in LDS); O^T (128 dims x 32 rows)
+//     tile (LDS) and the wave's Q rows (FP16, held in registers for the whole
+//     work-group), after one MFMA that adds the K offset's term; O^T (128 dims x 32 rows)
 //     += V^T P'^T is 8 more MFMAs whose B operand (P'^T) comes straight from
 //     the S^T accumulator registers, and whose A operand is read transposed
 //     from the [cell][dim] V tile (ds_read_b64_tr_b16) in the same cell order;
@@ -34,7 +35,7 @@
 //     S^T(c+1) chain with the softmax of chunk c between its MFMAs, so the
 //     matrix pipe and the VALU work at the same time;
 //   * K and V integers (plus the +1152 offset of the byte-to-FP16 trick) are
-//     exact in FP16; the K offset is removed by starting each S^T chain from
+//     exact in FP16; the K offset is removed by starting each S^T chain with
 //     -1152 sum(Q) of its row, k_scale * softmax_scale * log2(e) multiplies
 //     the score in FP32, and the FP16 probabilities are multiplied by the FP16
 //     v factor v_scale * 2^6 (2^-6 returns in the epilogue). Each lane tracks
@@ -69,8 +70,7 @@ constexpr int kD = 128;             // head dim
 constexpr int kQPerKv = 12;
 constexpr int kStages = 4;          // V tiles and factors: chunks c (read), c+1, c+2 (written)
 constexpr int kKStages = 2;         // K tiles: chunks c+1 (read), c+2 (written)
-constexpr int kRows = 8 * kQPerKv;  // rows of a work-group: 8 positions x 12 query heads
-constexpr int kKRow = kD + 8;       // K and Q tile rows: 128 dims + 16 bytes of padding
+constexpr int kKRow = kD + 8;       // K tile rows: 128 dims + 16 bytes of padding
 constexpr int kLead = 3;            // iterations between a read and its first use (producers)
 constexpr int kRing = 8;            // translated chunks (ring slots, indexed by chunk & 7)
 constexpr float kLazyLimit = 128.f;  // a lane's chunk probability sum, against the running maximum
@@ -93,7 +93,6 @@ struct __align__(16) Smem {
   float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
   _Float16 vf[kStages][kChunk];         // FP16(v_scale * 2^9); 0 where unusable
   uint32_t keep[kStages][4 * kChunk];   // keep masks, 16-byte units laid out by keep_unit()
-  _Float16 q[kRows * kKRow];            // the work-group's Q, [row][dim] in FP16, rows of kKRow
   Ring ring[kRing + 1];   // the last slot takes the upper producer lanes' copies
 };
 // two work-groups share a CU (LDS 160 KB): one's prologue and epilogue overlap
@@ -277,22 +276,31 @@ __device__ __forceinline__ void finish_translation(const PrefillArgs& a, const P
 
 // ---------------------------------------------------------------------------
 // Consumer waves 0..2: row block w (32 rows).
-// S^T (the chunk's 32 cells x this wave's 32 rows). qrow: this lane's row of
-// the Q tile, at dims 8hb (k-step ks reads dims 16ks + 8hb .. +7).
-__device__ __forceinline__ float16v scores_t(const Stage& st, const _Float16* qrow,
-                                             const float16v& s_init, int hb, int l32) {
-  float16v s = s_init;
-  const int cell = l32;
-  const _Float16* krow = st.k + cell * kKRow + 8 * hb;
+// The K tile holds k + 1152, so every S^T chain starts with an MFMA that adds
+// -1152 sum(Q) of each row: A has ones in k-slots 0 and 1 (lanes of half 0),
+// B the row's value split into two FP16 terms there (hi + lo, exact to FP32
+// precision), all other slots zero.
+__device__ __forceinline__ float16v offset_start(const half8& ones9, const half8& q9) {
+  float16v z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(ones9, q9, z, 0, 0, 0);
+}
+
+// S^T (the chunk's 32 cells x this wave's 32 rows). q: this lane's Q operands
+// (k-step ks: dims 16ks + 8hb .. +7 of its row), in registers for the whole
+// work-group.
+__device__ __forceinline__ float16v scores_t(const Stage& st, const half8 q[8], const half8& ones9,
+                                             const half8& q9, int hb, int l32) {
+  float16v s = offset_start(ones9, q9);
+  const _Float16* krow = st.k + l32 * kKRow + 8 * hb;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const half8 ka = *reinterpret_cast<const half8*>(krow + 16 * ks);
-    const half8 qb = *reinterpret_cast<const half8*>(qrow + 16 * ks);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb, s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, q[ks], s, 0, 0, 0);
   }
   return s;
 }
-
 // The A operand of O^T (dims 32mb + 0..31) += V^T P'^T for k-step ks, read
 // transposed from the [cell][dim] V tile with ds_read_b64_tr_b16: within each
 // group of 16 lanes, lane i receives element i % 4 of the 8-byte rows addressed
@@ -319,7 +327,8 @@ __device__ __forceinline__ half8 load_v_operand(const Stage& st, int ks, int mb,
 struct ConsState {
   float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^6
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
-  float16v s_init;    // -1152 sum(Q) of this lane's row, where every S^T chain starts
+  half8 q[8];          // this lane's Q operands (FP16), for every chunk
+  half8 ones9, q9;     // operands of the chain's first MFMA (adds -1152 sum(Q))
   half8 pb[2];        // P'^T of the previous chunk
   half8 vfrag[8];     // V^T operands of the previous chunk
   float m_run;        // running maximum (log2 domain) of this lane's row
@@ -367,22 +376,19 @@ __device__ __forceinline__ void prob_pair(ConsState& cs, const ChunkFactors& f, 
 }
 
 // The S^T(c+1) chain with the softmax of chunk c between its MFMAs (one
-// probability pair per MFMA); K and Q operands are read two MFMAs ahead, the
+// probability pair per MFMA); K operands are read two MFMAs ahead, the
 // remaining k factors on the way. Leaves P'^T(c) in cs.pb and returns this
 // lane's probability sum and P'^T sum.
 __device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, const _Float16* krow,
-                                              const _Float16* qrow, ChunkFactors& f,
-                                              half8 kfrag[8], half8 qfrag[8], float16v& s_next,
+                                              ChunkFactors& f, half8 kfrag[8], float16v& s_next,
                                               float& psum, float& lpc, int hb) {
   psum = 0.f;
   lpc = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], qfrag[j], j == 0 ? cs.s_init : s_next, 0, 0, 0);
-    if (j + 2 < 8) {
-      kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
-      qfrag[j + 2] = *reinterpret_cast<const half8*>(qrow + 16 * (j + 2));
-    }
+    if (j == 0) s_next = offset_start(cs.ones9, cs.q9);
+    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], cs.q[j], s_next, 0, 0, 0);
+    if (j + 2 < 8) kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
     const int r = 2 * j;
     prob_pair(cs, f, j, __builtin_fmaf(cs.s_cur[r], f.k4[r >> 2][r & 3], -cs.m_run),
               __builtin_fmaf(cs.s_cur[r + 1], f.k4[r >> 2][(r + 1) & 3], -cs.m_run), psum, lpc);
@@ -401,8 +407,7 @@ __device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, co
 // VALU work at the same time, forms P'^T(c) and reads chunk c's V^T operands
 // (their LDS latency passes during the barrier).
 template <int P>
-__device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Float16* qrow,
-                                             int hb, int l32) {
+__device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, int hb, int l32) {
   const Stage st = stage(sm, P);            // chunk c: factors, keep masks, V
   const Stage st_next = stage(sm, P + 1);   // chunk c+1: K
   const float ninf = -__builtin_inff();
@@ -417,19 +422,16 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   for (int j = 0; j < 8; ++j)
     cs.o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cs.vfrag[j], cs.pb[j >> 2], cs.o[j & 3], 0, 0, 0);
 
-  // the first two of chunk c+1's K operands and Q's (the others are read two
-  // MFMAs ahead of their use in the chain below)
-  half8 kfrag[8], qfrag[8];
+  // the first two of chunk c+1's K operands (the others are read two MFMAs
+  // ahead of their use in the chain below)
+  half8 kfrag[8];
   const _Float16* krow = st_next.k + l32 * kKRow + 8 * hb;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    kfrag[j] = *reinterpret_cast<const half8*>(krow + 16 * j);
-    qfrag[j] = *reinterpret_cast<const half8*>(qrow + 16 * j);
-  }
+  for (int j = 0; j < 2; ++j) kfrag[j] = *reinterpret_cast<const half8*>(krow + 16 * j);
 
   float16v s_next;
   float psum, lpc;
-  chain_softmax(cs, st, krow, qrow, f, kfrag, qfrag, s_next, psum, lpc, hb);
+  chain_softmax(cs, st, krow, f, kfrag, s_next, psum, lpc, hb);
 
   // the lazy stabiliser: only when some lane's chunk sum leaves [0, 128] is the
   // running maximum moved (what is accumulated is rescaled; this waits for the
@@ -477,19 +479,18 @@ __device__ __forceinline__ void consume_step(ConsState& cs, Smem& sm, const _Flo
   consumer_barrier();
 }
 
-__device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, const _Float16* qrow,
-                                               int hb, int l32, int nch) {
+__device__ __forceinline__ void consume_chunks(ConsState& cs, Smem& sm, int hb, int l32, int nch) {
   int c = 0;
   for (; c + 4 <= nch; c += 4) {
-    consume_step<0>(cs, sm, qrow, hb, l32);
-    consume_step<1>(cs, sm, qrow, hb, l32);
-    consume_step<2>(cs, sm, qrow, hb, l32);
-    consume_step<3>(cs, sm, qrow, hb, l32);
+    consume_step<0>(cs, sm, hb, l32);
+    consume_step<1>(cs, sm, hb, l32);
+    consume_step<2>(cs, sm, hb, l32);
+    consume_step<3>(cs, sm, hb, l32);
   }
   const int rem = nch - c;
-  if (rem > 0) consume_step<0>(cs, sm, qrow, hb, l32);
-  if (rem > 1) consume_step<1>(cs, sm, qrow, hb, l32);
-  if (rem > 2) consume_step<2>(cs, sm, qrow, hb, l32);
+  if (rem > 0) consume_step<0>(cs, sm, hb, l32);
+  if (rem > 1) consume_step<1>(cs, sm, hb, l32);
+  if (rem > 2) consume_step<2>(cs, sm, hb, l32);
 }
 
 __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, int h,
@@ -505,9 +506,9 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   const int qi = 8 * g + (row_n & 7);
   const bool row_ok = qi < a.n_q;
 
-  // Q in FP16 into the Q tile (the B operand of S^T = K Q^T is read from there:
-  // k-step s covers dims 16s..16s+15, lane half hb dims 16s + 8hb .. +7)
-  _Float16* qrow = sm.q + row_n * kKRow + 8 * hb;
+  ConsState cs;
+  // Q in FP16, straight into the B operands of S^T = K Q^T (k-step s: dims
+  // 16s + 8hb .. +7 of this lane's row)
   {
     const float* qg = a.q + ((int64_t)(row_ok ? qi : 0) * n_qh + h * kQPerKv + hq) * kD;
 #pragma unroll
@@ -515,16 +516,14 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
       float4v x0 = *reinterpret_cast<const float4v*>(qg + 16 * s + 8 * hb);
       float4v x1 = *reinterpret_cast<const float4v*>(qg + 16 * s + 8 * hb + 4);
       if (!row_ok) x0 = x1 = float4v{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<half8*>(qrow + 16 * s) =
-          half8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
-                (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+      cs.q[s] = half8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                      (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
     }
   }
 
-  lds_barrier();   // prologue: ring filled, Q tile stored
+  lds_barrier();   // prologue: ring filled
   lds_barrier();   // prologue: chunks 0 and 1 staged
 
-  ConsState cs;
   cs.m_run = kNoMax;
   cs.l_run = 0.f;
   cs.lp = 0.f;
@@ -541,20 +540,24 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 #pragma unroll
     for (int e = 0; e < 8; ++e) cs.pb[ks][e] = (_Float16)0.f;
   {
-    // -1152 times the sum of this lane's row of FP16 Q (both lane halves' dims)
+    // -1152 times the sum of this lane's row of FP16 Q (both lane halves'
+    // dims), as hi + lo in the first MFMA's operands
     const half2 one = {(_Float16)1.f, (_Float16)1.f};
     float qs = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const half8 x = *reinterpret_cast<const half8*>(qrow + 16 * s);
+    for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qs = __builtin_amdgcn_fdot2(half2{x[2 * e], x[2 * e + 1]}, one, qs, false);
-    }
+      for (int e = 0; e < 4; ++e)
+        qs = __builtin_amdgcn_fdot2(half2{cs.q[s][2 * e], cs.q[s][2 * e + 1]}, one, qs, false);
     const float init = -1152.f * (qs + __shfl_xor(qs, 32));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) cs.s_init[r] = init;
+    const _Float16 hi = (_Float16)init;
+    const _Float16 lo = (_Float16)(init - (float)hi);
+    const _Float16 zero = (_Float16)0.f, one1 = (_Float16)(hb == 0 ? 1.f : 0.f);
+    cs.ones9 = half8{one1, one1, zero, zero, zero, zero, zero, zero};
+    cs.q9 = hb == 0 ? half8{hi, lo, zero, zero, zero, zero, zero, zero}
+                    : half8{zero, zero, zero, zero, zero, zero, zero, zero};
   }
-  cs.s_cur = scores_t(stage(sm, 0), qrow, cs.s_init, hb, l32);
+  cs.s_cur = scores_t(stage(sm, 0), cs.q, cs.ones9, cs.q9, hb, l32);
   {
     // the running maximum starts at chunk 0's maximum over this row's chosen
     // cells, so that the first chunk needs no rescale (the sinks lead the union)
@@ -574,7 +577,7 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
   }
   lds_barrier();   // prologue: chunk 0's K tile read (the producers rewrite it next)
 
-  consume_chunks(cs, sm, qrow, hb, l32, nch);
+  consume_chunks(cs, sm, hb, l32, nch);
   // the last chunk's O^T update
 #pragma unroll
   for (int j = 0; j < 8; ++j)
