@@ -133,6 +133,24 @@ def test_attention_random_selections_all_rows(seed, n_ctx, n_q, n_kv, dup, nonre
     assert np.all(out[empty] == 0)
 
 
+def test_attention_empty_groups_and_chunk_remainders():
+    """Groups whose union is empty (every position selected nothing: the chunk
+    loop runs zero times) next to groups whose unions end in every position of
+    a 4-chunk unroll; rows without a resident chosen cell output 0."""
+    print("case empty groups", flush=True)
+    d = synth.small_random(41, n_ctx=2600, n_q=40, n_kv=2, max_len=300)
+    sel, sel_len = d["sel"].copy(), d["sel_len"].copy()
+    sel_len[8:16] = 0                     # group 1: empty union
+    sel[8:16] = -1
+    sel_len[30] = 0                       # one empty position inside group 3
+    sel[30] = -1
+    for j, n in zip(range(16, 24), (1, 33, 65, 97, 3, 40, 70, 100)):
+        sel_len[j] = min(n, int(sel_len[j]))   # group 2: short rows
+    d["sel"], d["sel_len"] = sel, sel_len
+    out = _check_problem(d, what="empty groups")
+    assert np.all(out[8:16] == 0) and np.all(out[30] == 0)
+
+
 def test_attention_exact_mean_catches_single_cell_errors():
     """k_scale = 0 and v_scale = 2^-6: every logit is exactly 0, so every chosen
     probability is exactly 1 in FP16 and the sums are exact in FP32; the output
