@@ -11,6 +11,9 @@ Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
 
 Every function here is pinned by tests/test_oracle_pins.py against dense
 brute force, closed forms and invariants; none is "parity unpinned".
+
+The selection step before the path (block scores -> selection rows) lives in
+oracle/selection.py (numpy), pinned by tests/test_selection_oracle.py.
 """
 from __future__ import annotations
 

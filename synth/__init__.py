@@ -245,3 +245,32 @@ def as_problem(inputs: dict) -> dict:
     d = dict(inputs)
     d.update(n_ctx=w.n_ctx, n_q=w.n_q, n_kv=w.n_kv, n_pages=w.pool_pages, sel_cap=w.sel_cap)
     return d
+
+
+def block_scores(n_q: int, n_ctx: int, rho: float, seed: int,
+                 levels: Optional[int] = None) -> np.ndarray:
+    """Seeded per-position block scores for the selection step.
+
+    float32 [n_q][ceil(n_ctx/64)]. The page does not say how blocks are scored,
+    so these stand in for the model's scores:
+    - each block's score follows a Gaussian AR(1) walk over the positions,
+      s_j = rho * s_(j-1) + sqrt(1 - rho^2) * e_j;
+    - rho near 1 gives neighbouring positions nearly the same top blocks,
+      while rho = 0 draws every position independently;
+    - with `levels`, scores are quantised to the integers 0 .. levels-1,
+      which gives many exact ties.
+    Row j scores every block; the selection reads only the blocks before the
+    position's own block.
+    """
+    rng = np.random.default_rng(seed)
+    nb = -(-n_ctx // PAGE_SIZE)
+    out = np.empty((n_q, nb), np.float32)
+    s = rng.standard_normal(nb)
+    c = math.sqrt(max(0.0, 1.0 - rho * rho))
+    for j in range(n_q):
+        if j:
+            s = rho * s + c * rng.standard_normal(nb)
+        out[j] = s
+    if levels is not None:
+        out = np.floor((out + 3.0) * (levels / 6.0)).clip(0, levels - 1).astype(np.float32)
+    return out

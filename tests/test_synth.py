@@ -104,3 +104,16 @@ def test_small_random_edge_features():
                    for j in range(37))
     assert dup_rows > 0
     assert d["sel_len"].max() <= 2051
+
+
+def test_block_scores_recipe():
+    a = synth.block_scores(200, 5000, 0.9, seed=3)
+    b = synth.block_scores(200, 5000, 0.9, seed=3)
+    assert a.shape == (200, 79) and a.dtype == np.float32
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # AR(1): lag-1 correlation near rho, unit variance
+    x, y = a[:-1].ravel().astype(np.float64), a[1:].ravel().astype(np.float64)
+    assert abs(np.corrcoef(x, y)[0, 1] - 0.9) < 0.03
+    assert abs(a.std() - 1.0) < 0.1
+    t = synth.block_scores(50, 640, 0.0, seed=4, levels=3)
+    assert set(np.unique(t).tolist()) <= {0.0, 1.0, 2.0}
