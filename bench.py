@@ -11,6 +11,10 @@ Prints ONE JSON line: the metric (selected query-head-cells per second; prompt
 positions per second beside it), the roofline of the dominant kernel measured
 with HIP events on its own stream, and the CPU oracle timed on a bounded sample
 of the same workload on this host's cores.
+
+`--op select` measures the step before the path instead: block scores -> the
+selection rows (top 31 earlier blocks + 3 sinks + own block) of the same
+chunk's positions, one kernel launch per step. It prints its own JSON line.
 """
 from __future__ import annotations
 
@@ -35,6 +39,10 @@ UNION_KV_BYTES = 264
 UNION_CELL_BYTES = UNION_KV_BYTES + 4 + 1 + 4
 ROW_BYTES = 128 * 4 * 2        # q in + out, per (query position, query head)
 FLOP_PER_CELL_ROW = 4 * 128    # QK^T and PV, per (union cell, row)
+SELECT_RHO = 0.99              # AR(1) correlation of the block scores across positions
+# the kernel each op's roofline and counter summary is about
+OP_KERNELS = {"path": ("sel_attn_prefill_kernel", "union_build_kernel"),
+              "select": ("select_blocks_kernel",)}
 
 
 def parse():
@@ -43,6 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ctx32k_drift005")
+    ap.add_argument("--op", choices=("path", "select"), default="path",
+                    help="path: union + attention (the default); select: the selection step")
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="query positions of the oracle's timed sample (-1 = all of the chunk, 0 = skip)")
     ap.add_argument("--profile", action="store_true",
@@ -62,10 +72,17 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload_name: str):
-    """HBM bytes per prefill launch from the committed counter summary, if it was
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "prefill_%s_counters.json" % workload_name)
+def _profile_names(workload: str, op: str):
+    """(stats text, counter json) file names under profiles/ for an op."""
+    if op == "path":
+        return "kernels_%s_stats.txt" % workload, "prefill_%s_counters.json" % workload
+    return "kernels_%s_%s_stats.txt" % (op, workload), "%s_%s_counters.json" % (op, workload)
+
+
+def counter_traffic(workload_name: str, op: str = "path"):
+    """HBM bytes per launch of the op's main kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", _profile_names(workload_name, op)[1])
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -91,15 +108,18 @@ def _short(name: str) -> str:
     return name.split("(")[0].split("<")[0].split("::")[-1]
 
 
-def summarize(d: str, workload: str):
+def summarize(d: str, workload: str, op: str = "path"):
     """Summaries of a profile.sh run: the kernel-trace statistics as text, and the
-    HBM bytes per prefill launch from FETCH_SIZE / WRITE_SIZE, each counter scaled
-    by what it reads for a copy of COPY_BYTES (the copy kernel with the largest
-    grid in the run)."""
+    HBM bytes per launch of the op's kernels from FETCH_SIZE / WRITE_SIZE, each
+    counter scaled by what it reads for a copy of COPY_BYTES (the copy kernel
+    with the largest grid in the run)."""
+    stats_name, counters_name = _profile_names(workload, op)
+    kernels = OP_KERNELS[op]
     with open(os.path.join(d, "commands.txt")) as f:
         commands = f.read().strip().splitlines()
     stats = _csv_rows(os.path.join(d, "trace", "run_kernel_stats.csv"))
-    lines = ["rocprofv3 --kernel-trace --stats summary, workload %s" % workload,
+    lines = ["rocprofv3 --kernel-trace --stats summary, workload %s%s" % (
+                 workload, "" if op == "path" else ", op " + op),
              "command: " + commands[0], "",
              "%-28s %6s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "total_%")]
     for r in stats:
@@ -107,7 +127,7 @@ def summarize(d: str, workload: str):
             _short(r["Name"])[:28], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "kernels_%s_stats.txt" % workload), "w") as f:
+    with open(os.path.join(ROOT, "profiles", stats_name), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     rec = {"workload": workload, "source_hash": source_hash(), "commands": commands[1:3],
@@ -120,15 +140,15 @@ def summarize(d: str, workload: str):
         copy_kib = np.mean([float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == big])
         factor = COPY_BYTES / (copy_kib * 1024.0)
         rec[counter] = {"copy_KiB": copy_kib, "factor": factor}
-        for k in ("sel_attn_prefill_kernel", "union_build_kernel"):
+        for k in kernels:
             v = [float(r["Counter_Value"]) for r in rows if _short(r["Kernel_Name"]) == k]
             ent = rec["kernels"].setdefault(k, {})
             ent[counter + "_KiB_per_dispatch"] = float(np.mean(v))
             ent[counter.split("_")[0].lower() + "_bytes"] = float(np.mean(v)) * 1024.0 * factor
     for ent in rec["kernels"].values():
         ent["hbm_bytes"] = ent["fetch_bytes"] + ent["write_bytes"]
-    rec["hbm_bytes_per_launch"] = rec["kernels"]["sel_attn_prefill_kernel"]["hbm_bytes"]
-    with open(os.path.join(ROOT, "profiles", "prefill_%s_counters.json" % workload), "w") as f:
+    rec["hbm_bytes_per_launch"] = rec["kernels"][kernels[0]]["hbm_bytes"]
+    with open(os.path.join(ROOT, "profiles", counters_name), "w") as f:
         json.dump(rec, f, indent=1)
     lines += ["", "HBM bytes per dispatch from counters (two --pmc runs, one counter each):"]
     lines += ["command: " + c for c in commands[1:3]]
@@ -142,17 +162,20 @@ def summarize(d: str, workload: str):
             ent["WRITE_SIZE_KiB_per_dispatch"], ent["write_bytes"] / 1e6, ent["hbm_bytes"] / 1e6))
     lines.append("kernel sources: sha256 prefix %s (the benchmark uses these bytes only while it "
                  "matches)" % rec["source_hash"])
-    lines.append("made by: bash profile.sh OUTDIR; python3 bench.py --summarize OUTDIR")
-    with open(os.path.join(ROOT, "profiles", "kernels_%s_stats.txt" % workload), "w") as f:
+    extra = ("" if op == "path" else " --op " + op) + \
+        ("" if workload == "ctx32k_drift005" else " --workload " + workload)
+    lines.append("made by: bash profile.sh OUTDIR%s; python3 bench.py --summarize OUTDIR%s" % (
+        extra, extra))
+    with open(os.path.join(ROOT, "profiles", stats_name), "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(open(os.path.join(ROOT, "profiles", "kernels_%s_stats.txt" % workload)).read())
+    print(open(os.path.join(ROOT, "profiles", stats_name)).read())
     print(json.dumps(rec, indent=1))
 
 
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize, args.workload)
+        summarize(args.summarize, args.workload, args.op)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -166,6 +189,9 @@ def main():
     import sparse_top_selection_amd as sa
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.op == "select":
+        bench_select(args)
+        return
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
     inp = synth.as_problem(synth.generate(w))
@@ -301,6 +327,110 @@ def main():
         }
         result["parity_on_cpu_sample"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
                                           "out_rms": float(np.sqrt(np.mean(ref ** 2)))}
+    print(json.dumps(result), flush=True)
+
+
+def bench_select(args):
+    """The selection step on the chunk's positions: one launch per step.
+
+    A launch takes about as long as the host needs to enqueue it, so the timed
+    launches are queued behind device copies that outlast the enqueueing. One pair of HIP events
+    on the launch stream then brackets all K launches, which run back to back,
+    and the average launch time is their span divided by K.
+    """
+    import torch
+    import synth
+    import sparse_top_selection_amd as sa
+
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    first = w.n_ctx - w.n_q
+    scores_np = synth.block_scores(w.n_q, w.n_ctx, SELECT_RHO, seed=w.seed)
+    scores = torch.from_numpy(scores_np).to(dev)
+    sel = torch.empty((w.n_q, w.sel_cap), dtype=torch.int32, device=dev)
+    sel_len = torch.empty(w.n_q, dtype=torch.int32, device=dev)
+    dims = sa.make_dims(w.n_ctx, w.n_q, 1, 1, sel_cap=w.sel_cap)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        sa.sel_attn_select_blocks(dims, first, scores, sel, sel_len, stream)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    steps = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not args.profile:   # the counter runs calibrate on the one copy size below
+        busy_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        busy_dst = torch.empty_like(busy_src)
+        torch.cuda.synchronize()
+        for _ in range(8 + steps // 8):   # ~0.2 ms each; enqueueing a launch takes ~25 us
+            busy_dst.copy_(busy_src)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = e0.elapsed_time(e1) / steps
+
+    lens = sel_len.cpu().numpy().astype(np.int64)
+    own = np.arange(first, w.n_ctx) // 64
+    read_bytes = 4 * int(np.where(own > 31, own, 0).sum())   # the scores the kernel reads
+    write_bytes = 4 * int(lens.sum()) + 4 * w.n_q            # rows and lengths
+    alg_bytes = read_bytes + write_bytes
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+
+    if args.profile:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": "selection rows/s (positions of the 32K-context prompt chunk, from block scores)",
+        "value": w.n_q / (kern_ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": kern_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 scores, int32 cells",
+        "data": "synthetic (seeded AR(1) block scores, rho %.2f)" % SELECT_RHO,
+        "config": {"workload": "select_" + w.name, "n_ctx": w.n_ctx, "query_positions": w.n_q,
+                   "first_position": first, "blocks": -(-w.n_ctx // 64), "sel_cap": w.sel_cap,
+                   "parallelism": "single GPU"},
+        "timing": "one HIP event pair around K back-to-back launches queued behind device copies",
+        "mean_sel_len": float(lens.mean()),
+        "roofline": {
+            "kernel": "select_blocks_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": counter_traffic(w.name, "select"),
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+        "source_hash": source_hash(),
+    }
+    if args.cpu_rows != 0 and not args.profile:
+        from oracle import selection as S
+        n_rows = w.n_q if args.cpu_rows < 0 else min(args.cpu_rows, w.n_q)
+        c0 = time.perf_counter()
+        ref, ref_len = S.select_blocks(scores_np[:n_rows], first, w.n_ctx, w.sel_cap)
+        cpu_s = time.perf_counter() - c0
+        got = sel[:n_rows].cpu().numpy()
+        valid = np.arange(w.sel_cap)[None, :] < ref_len[:, None]
+        same = bool(np.array_equal(lens[:n_rows], ref_len) and np.array_equal(got[valid], ref[valid]))
+        result["cpu_baseline"] = {
+            "value": n_rows / cpu_s, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": "positions %d..%d (%d rows), numpy per-row sort, %.1f s" % (
+                first, first + n_rows - 1, n_rows, cpu_s)}
+        result["parity_on_cpu_sample"] = {"rows_bit_exact": same}
     print(json.dumps(result), flush=True)
 
 

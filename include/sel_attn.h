@@ -18,6 +18,8 @@
  * One pass of the path is two calls on one stream:
  *   sel_attn_build_union  selections -> per-group union, masks, lengths
  *   sel_attn_prefill      union + q + paged INT8 K/V -> attention output
+ * and the step before it, when the selections come from block scores:
+ *   sel_attn_select_blocks  block scores -> per-position selections
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -64,6 +66,10 @@ extern "C" {
 #define SEL_ATTN_PAGE_SIZE 64
 #define SEL_ATTN_Q_PER_KV 12
 #define SEL_ATTN_GROUP 8           /* positions per union group */
+#define SEL_ATTN_SINKS 3           /* sink cells 0, 1, 2 in every selection */
+#define SEL_ATTN_TOP_BLOCKS 31     /* earlier blocks a selection takes by score */
+#define SEL_ATTN_SEL_MAX 2051      /* 3 + 31*64 + 64: cells in a full selection */
+#define SEL_ATTN_SELECT_MAX_CTX 262144 /* n_ctx limit of sel_attn_select_blocks */
 
 typedef struct sel_attn_dims {
   int32_t n_ctx;     /* logical context length in cells, >= 1; page_table has
@@ -81,6 +87,33 @@ typedef struct sel_attn_dims {
   int32_t n_pages;   /* physical pages in each pool, >= 1; a pool
                         (n_pages * n_kv * 64 * 128 bytes) must stay under 4 GiB */
 } sel_attn_dims;
+
+/*
+ * sel_attn_select_blocks - the selection step before the path (section What
+ * changed: the selection, block scores then top-k, which the page leaves as it
+ * is; section Accuracy: a selection holds at most 2,051 cells). The page does
+ * not say how blocks are scored; the scores are an input.
+ *
+ *   first_pos     position of query index 0; query index j is at position
+ *                 p = first_pos + j, and 0 <= first_pos, first_pos + n_q <= n_ctx
+ *   block_scores  const float [n_q][ceil(n_ctx/64)]  row j scores the blocks
+ *                 before p's own block, floor(p/64); later entries are not read
+ *   sel           int32 [n_q][sel_cap]   out: row j in ascending order
+ *   sel_len       int32 [n_q]            out: cells in row j
+ *   Row j is the sink cells {0, 1, 2}, the 31 earlier blocks (64 cells each)
+ *   with the highest scores, and the own block's cells up to p. A position with
+ *   at most 31 earlier blocks takes all of them: its row is [0, p]. Equal scores
+ *   go to the lower block index first; a NaN score counts as -inf; -0.0 equals
+ *   +0.0. Each cell appears once (the sinks lie inside block 0 when it is
+ *   chosen), so sel_len[j] <= 2051. Entries past sel_len[j] are left untouched.
+ *   The output feeds sel_attn_build_union with the same dims.
+ *   Errors (nothing enqueued): sel_cap < 2051 or positions outside [0, n_ctx)
+ *   give EINVAL; n_ctx > SEL_ATTN_SELECT_MAX_CTX gives EUNSUPPORTED. The
+ *   n_kv and n_pages fields are checked as for the other calls but not used.
+ *   Alignment: 4 bytes for every array.
+ */
+int sel_attn_select_blocks(const sel_attn_dims* d, int32_t first_pos, const float* block_scores,
+                           int32_t* sel, int32_t* sel_len, hipStream_t stream);
 
 /*
  * sel_attn_build_union - the union step (section Summary: a first kernel builds,

@@ -6,10 +6,11 @@ kernels; PyTorch provides device memory and the current stream. There is no
 fallback: importing this package fails loudly when libselattn.so is missing,
 and every call raises when the library returns an error code.
 
-The functions named like the C entry points (sel_attn_build_union,
-sel_attn_prefill, sel_attn_last_error) take preallocated device tensors and
-mirror include/sel_attn.h one to one. build_union(), prefill() and
-check_status() are conveniences that allocate outputs and read the status word.
+The functions named like the C entry points (sel_attn_select_blocks,
+sel_attn_build_union, sel_attn_prefill, sel_attn_last_error) take preallocated
+device tensors and mirror include/sel_attn.h one to one. select_blocks(),
+build_union(), prefill() and check_status() are conveniences that allocate
+outputs and read the status word.
 
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
 (opt-in STRATA_PROMPT_ATTN_UNION=1)", section Summary.
@@ -46,8 +47,13 @@ HEAD_DIM = 128
 PAGE_SIZE = 64
 Q_PER_KV = 12
 GROUP = 8
+SINKS = 3
+TOP_BLOCKS = 31
+SEL_MAX = 2051
+SELECT_MAX_CTX = 262144
 
-EXPORTED = ("sel_attn_build_union", "sel_attn_prefill", "sel_attn_last_error")
+EXPORTED = ("sel_attn_select_blocks", "sel_attn_build_union", "sel_attn_prefill",
+            "sel_attn_last_error")
 
 
 class Dims(ctypes.Structure):
@@ -64,6 +70,8 @@ def make_dims(n_ctx: int, n_q: int, n_kv: int, n_pages: int, sel_cap: int = 2051
 
 
 _p = ctypes.c_void_p
+_lib.sel_attn_select_blocks.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, _p, _p, _p, _p]
+_lib.sel_attn_select_blocks.restype = ctypes.c_int
 _lib.sel_attn_build_union.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p]
 _lib.sel_attn_build_union.restype = ctypes.c_int
 _lib.sel_attn_prefill.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -102,6 +110,13 @@ def _stream(stream) -> Optional[int]:
 def _check(rc: int):
     if rc != OK:
         raise SelAttnError(rc, sel_attn_last_error())
+
+
+def sel_attn_select_blocks(dims: Dims, first_pos: int, block_scores, sel, sel_len,
+                           stream=None) -> None:
+    """Enqueue the selection step (see include/sel_attn.h). Tensors or raw device pointers."""
+    _check(_lib.sel_attn_select_blocks(ctypes.byref(dims), int(first_pos), _ptr(block_scores),
+                                       _ptr(sel), _ptr(sel_len), _stream(stream)))
 
 
 def sel_attn_build_union(dims: Dims, sel, sel_len, union_cells, union_mask, union_len, status,
@@ -151,6 +166,31 @@ def check_status(status: torch.Tensor) -> int:
                                 ("UNION_LEN", 8), ("V_SCALE", 16)) if v & b]
         raise SelAttnError(v, "device status: " + "|".join(names))
     return v
+
+
+def select_blocks(block_scores: torch.Tensor, first_pos: int, n_ctx: int,
+                  sel_cap: int = SEL_MAX, stream=None, out=None):
+    """Selections of positions first_pos .. first_pos + n_q - 1 from block
+    scores float32 [n_q][ceil(n_ctx/64)]. Returns (sel, sel_len); entries past
+    sel_len are left as allocated (torch.empty) or as they were in `out`."""
+    dev = block_scores.device
+    _need(block_scores, "block_scores", torch.float32, 2, None)
+    n_q, nb = block_scores.shape
+    if nb != -(-n_ctx // PAGE_SIZE):
+        raise ValueError("block_scores must be [n_q][ceil(n_ctx/64)]")
+    if out is None:
+        sel = torch.empty((n_q, sel_cap), dtype=torch.int32, device=dev)
+        sel_len = torch.empty(n_q, dtype=torch.int32, device=dev)
+    else:
+        sel, sel_len = out
+        _need(sel, "sel", torch.int32, 2, dev)
+        _need(sel_len, "sel_len", torch.int32, 1, dev)
+        if sel.shape[0] != n_q or sel_len.shape[0] != n_q:
+            raise ValueError("sel and sel_len must have n_q rows")
+        sel_cap = sel.shape[1]
+    dims = make_dims(n_ctx, n_q, 1, 1, sel_cap=sel_cap)
+    sel_attn_select_blocks(dims, first_pos, block_scores, sel, sel_len, stream)
+    return sel, sel_len
 
 
 def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, status=None, stream=None,

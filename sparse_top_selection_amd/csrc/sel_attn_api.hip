@@ -90,6 +90,43 @@ extern "C" {
 
 const char* sel_attn_last_error(void) { return g_err; }
 
+int sel_attn_select_blocks(const sel_attn_dims* d, int32_t first_pos, const float* block_scores,
+                           int32_t* sel, int32_t* sel_len, hipStream_t stream) {
+  static const char* who = "sel_attn_select_blocks";
+  int rc = check_dims(d, who);
+  if (rc) return rc;
+  if (d->sel_cap < SEL_ATTN_SEL_MAX)
+    return fail(SEL_ATTN_EINVAL, "%s: sel_cap %d cannot hold a full selection (%d cells)", who,
+                d->sel_cap, SEL_ATTN_SEL_MAX);
+  if (d->n_ctx > SEL_ATTN_SELECT_MAX_CTX)
+    return fail(SEL_ATTN_EUNSUPPORTED, "%s: n_ctx %d above %d", who, d->n_ctx,
+                SEL_ATTN_SELECT_MAX_CTX);
+  if (first_pos < 0 || (int64_t)first_pos + d->n_q > d->n_ctx)
+    return fail(SEL_ATTN_EINVAL, "%s: positions [%d, %lld) outside [0, n_ctx=%d)", who, first_pos,
+                (long long)first_pos + d->n_q, d->n_ctx);
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
+  if (!block_scores || !sel || !sel_len) return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
+  if (!aligned(block_scores, 4) || !aligned(sel, 4) || !aligned(sel_len, 4))
+    return fail(SEL_ATTN_EINVAL, "%s: arrays must be 4-byte aligned", who);
+  rc = check_device(who);
+  if (rc) return rc;
+  selattn::SelectArgs a;
+  a.scores = block_scores;
+  a.sel = sel;
+  a.sel_len = sel_len;
+  a.n_q = d->n_q;
+  a.first_pos = first_pos;
+  a.n_blocks = (d->n_ctx + SEL_ATTN_PAGE_SIZE - 1) / SEL_ATTN_PAGE_SIZE;
+  a.sel_cap = d->sel_cap;
+  hipError_t e = selattn::launch_select_blocks(a, stream);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SEL_ATTN_OK;
+}
+
 int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32_t* sel_len,
                          int32_t* union_cells, uint8_t* union_mask, int32_t* union_len,
                          uint32_t* status, hipStream_t stream) {

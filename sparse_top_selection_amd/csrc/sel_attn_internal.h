@@ -42,6 +42,17 @@ struct PrefillArgs {
   int32_t per_xcd;     // workgroups each XCD walks through (grid = 8 * per_xcd)
 };
 
+struct SelectArgs {
+  const float* scores;   // [n_q][n_blocks]
+  int32_t* sel;          // [n_q][sel_cap]
+  int32_t* sel_len;      // [n_q]
+  int32_t n_q;
+  int32_t first_pos;     // position of query index 0
+  int32_t n_blocks;      // ceil(n_ctx / 64): the score row stride
+  int32_t sel_cap;
+};
+
+hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_union_build(const UnionArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["sel_attn_build_union", "sel_attn_last_error",
-                                    "sel_attn_prefill"]
+                                    "sel_attn_prefill", "sel_attn_select_blocks"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -62,6 +62,30 @@ def test_bad_dims_rejected_on_host(kw, code):
         sa.sel_attn_prefill(_dims(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             0.1, FAKE, FAKE, stream=0)
     assert e.value.code == code
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_select_blocks(_dims(sel_cap=2051, **kw) if "sel_cap" not in kw else _dims(**kw),
+                                  0, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("kw,first,code", [
+    (dict(sel_cap=2050), 0, -1),                      # cannot hold a full selection
+    (dict(sel_cap=2051, n_ctx=1024, n_q=16), 1009, -1),   # last position past n_ctx
+    (dict(sel_cap=2051), -1, -1),                     # negative first position
+    (dict(sel_cap=2051, n_ctx=262145, n_q=16, n_pages=4200), 0, -2),   # context over the limit
+])
+def test_select_blocks_rejects_on_host(kw, first, code):
+    import sparse_top_selection_amd as sa
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_select_blocks(_dims(**kw), first, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == code
+    assert "sel_attn_select_blocks" in sa.sel_attn_last_error()
+    if code == -1 and kw.get("sel_cap") == 2051 and first >= 0:
+        # the same call one position earlier passes the position check and
+        # fails only at a NULL pointer
+        with pytest.raises(sa.SelAttnError) as e:
+            sa.sel_attn_select_blocks(_dims(**kw), first - 1, FAKE, None, FAKE, stream=0)
+        assert "NULL" in sa.sel_attn_last_error()
 
 
 def test_null_and_misaligned_pointers_rejected_on_host():
@@ -91,4 +115,7 @@ def test_empty_query_batch_is_a_no_op():
     sa.sel_attn_build_union(_dims(n_q=0), None, None, None, None, None, FAKE, stream=0)
     sa.sel_attn_prefill(_dims(n_q=0), None, None, None, None, None, None, None, None, None, 0.1,
                         None, FAKE, stream=0)
+    sa.sel_attn_select_blocks(_dims(n_q=0, sel_cap=2051), 5, None, None, None, stream=0)
     assert sa.sel_attn_last_error() == ""
+    with pytest.raises(sa.SelAttnError):   # misaligned scores
+        sa.sel_attn_select_blocks(_dims(sel_cap=2051), 0, FAKE + 2, FAKE, FAKE, stream=0)
