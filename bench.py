@@ -19,6 +19,7 @@ chunk's positions, one kernel launch per step. It prints its own JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -53,6 +54,11 @@ def parse():
     ap.add_argument("--workload", default="ctx32k_drift005")
     ap.add_argument("--op", choices=("path", "select"), default="path",
                     help="path: union + attention (the default); select: the selection step")
+    ap.add_argument("--sel", metavar="FILE",
+                    help="replay recorded selections (.npz from synth.save_selections) instead of "
+                         "the workload's own; n_ctx and n_q come from the file")
+    ap.add_argument("--kv-resident", type=float, default=1.0, metavar="F",
+                    help="fraction of logical pages resident; the rest are marked -1 (seeded)")
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="query positions of the oracle's timed sample (-1 = all of the chunk, 0 = skip)")
     ap.add_argument("--profile", action="store_true",
@@ -194,7 +200,20 @@ def main():
         return
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
-    inp = synth.as_problem(synth.generate(w))
+    label = w.name
+    if args.sel:
+        rec = synth.load_selections(args.sel)
+        w = dataclasses.replace(w, n_ctx=rec["n_ctx"], n_q=rec["sel"].shape[0],
+                                sel_cap=rec["sel"].shape[1])
+        inp = synth.generate(w, with_sel=False)
+        inp["sel"], inp["sel_len"] = rec["sel"], rec["sel_len"]
+        label = "replay:%s (pools of %s)" % (os.path.basename(args.sel), label)
+    else:
+        inp = synth.generate(w)
+    inp = synth.as_problem(inp)
+    if args.kv_resident < 1.0:
+        inp["page_table"] = synth.drop_pages(inp["page_table"], args.kv_resident, seed=w.seed)
+        label += " resident %.2f" % args.kv_resident
 
     # work counts of this input
     sel, sel_len, pt = inp["sel"], inp["sel_len"], inp["page_table"]
@@ -252,7 +271,8 @@ def main():
     union_kv_bytes = union_cells * w.n_kv * UNION_KV_BYTES
     flops = union_cells * w.n_kv * 96 * FLOP_PER_CELL_ROW
     achieved = alg_bytes / (prefill_ms * 1e-3) / 1e9
-    traffic = counter_traffic(w.name)
+    # the committed counters were taken on the workload's own inputs
+    traffic = None if (args.sel or args.kv_resident < 1.0) else counter_traffic(w.name)
 
     if args.profile:
         # plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
@@ -276,7 +296,7 @@ def main():
         "dtype": "int8 K/V, fp16 products, fp32 softmax and sums",
         "data": "synthetic (seeded; shapes of the pages' parity self-test)",
         "config": {
-            "workload": w.name,
+            "workload": label,
             "n_ctx": w.n_ctx, "query_positions": w.n_q, "first_position": w.first_pos,
             "kv_heads": w.n_kv, "q_heads_per_kv": w.q_per_kv, "head_dim": w.head_dim,
             "page_size": w.page_size, "pool_pages": w.pool_pages, "sel_cap": w.sel_cap,

@@ -146,12 +146,14 @@ def _selection_rows(rng: np.random.Generator, w: Workload, positions: np.ndarray
     return rows
 
 
-def generate(w: Workload, with_q: bool = True, with_pools: bool = True) -> dict:
+def generate(w: Workload, with_q: bool = True, with_pools: bool = True,
+             with_sel: bool = True) -> dict:
     """Draw every input of one workload from SeedSequence(w.seed).
 
     Streams, in order: page table, K/V pools, scales, q, selections. Skipping the
-    pools or q (for tests that only need selections) leaves the other streams
-    unchanged because each stream is spawned separately.
+    pools, q or the selections (for tests that only need the rest, or a replay
+    that brings its own selections) leaves the other streams unchanged because
+    each stream is spawned separately.
     """
     ss = np.random.SeedSequence(w.seed).spawn(5)
     r_pt, r_kv, r_sc, r_q, r_sel = (np.random.default_rng(s) for s in ss)
@@ -172,6 +174,10 @@ def generate(w: Workload, with_q: bool = True, with_pools: bool = True) -> dict:
         out["q"] = r_q.standard_normal((w.n_q, w.n_qh, w.head_dim), dtype=np.float32)
 
     positions = np.arange(w.first_pos, w.n_ctx)
+    out["positions"] = positions.astype(np.int64)
+    out["softmax_scale"] = np.float32(1.0 / math.sqrt(w.head_dim))
+    if not with_sel:
+        return out
     rows = _selection_rows(r_sel, w, positions)
     sel = np.full((w.n_q, w.sel_cap), -1, dtype=np.int32)
     sel_len = np.zeros(w.n_q, dtype=np.int32)
@@ -182,8 +188,6 @@ def generate(w: Workload, with_q: bool = True, with_pools: bool = True) -> dict:
         sel_len[j] = cells.size
     out["sel"] = sel
     out["sel_len"] = sel_len
-    out["positions"] = positions.astype(np.int64)
-    out["softmax_scale"] = np.float32(1.0 / math.sqrt(w.head_dim))
     return out
 
 
@@ -273,4 +277,52 @@ def block_scores(n_q: int, n_ctx: int, rho: float, seed: int,
         out[j] = s
     if levels is not None:
         out = np.floor((out + 3.0) * (levels / 6.0)).clip(0, levels - 1).astype(np.float32)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Recorded selections and partial residency. The page's timing tool replays a
+# selection dump and its notes name a partly resident KV pool as untested
+# (section What changed, the parity test's arguments; section Extra Notes).
+# No dump from a real model is available here, so files are written from the
+# generators above; the format is plain arrays that numpy reads without pickle.
+# ----------------------------------------------------------------------------
+def save_selections(path: str, sel: np.ndarray, sel_len: np.ndarray, n_ctx: int,
+                    first_pos: int) -> None:
+    """Write selections as an .npz: sel int32 [n_q][cap], sel_len int32 [n_q],
+    n_ctx and first_pos (query index j is at position first_pos + j)."""
+    np.savez(path, sel=np.ascontiguousarray(sel, np.int32),
+             sel_len=np.ascontiguousarray(sel_len, np.int32),
+             n_ctx=np.int64(n_ctx), first_pos=np.int64(first_pos))
+
+
+def load_selections(path: str) -> dict:
+    """Read a file written by save_selections (no pickle) and check its shapes
+    and ranges: lengths in [0, cap], entries in [0, n_ctx), entries causal."""
+    with np.load(path, allow_pickle=False) as f:
+        sel = np.ascontiguousarray(f["sel"], np.int32)
+        sel_len = np.ascontiguousarray(f["sel_len"], np.int32)
+        n_ctx = int(f["n_ctx"])
+        first_pos = int(f["first_pos"])
+    if sel.ndim != 2 or sel_len.shape != (sel.shape[0],):
+        raise ValueError("sel must be [n_q][cap] and sel_len [n_q]")
+    n_q, cap = sel.shape
+    if first_pos < 0 or first_pos + n_q > n_ctx:
+        raise ValueError("positions outside [0, n_ctx)")
+    if np.any(sel_len < 0) or np.any(sel_len > cap):
+        raise ValueError("a length outside [0, cap]")
+    valid = np.arange(cap)[None, :] < sel_len[:, None]
+    pos = (first_pos + np.arange(n_q))[:, None]
+    if np.any(valid & ((sel < 0) | (sel > pos))):
+        raise ValueError("an entry outside [0, p]")
+    return {"sel": sel, "sel_len": sel_len, "n_ctx": n_ctx, "first_pos": first_pos}
+
+
+def drop_pages(page_table: np.ndarray, resident: float, seed: int) -> np.ndarray:
+    """A copy of the page table in which a seeded random (1 - resident)
+    fraction of the logical pages is marked not resident (-1)."""
+    rng = np.random.default_rng(seed)
+    out = page_table.copy()
+    n_off = int(round((1.0 - resident) * out.size))
+    out[rng.choice(out.size, size=n_off, replace=False)] = -1
     return out

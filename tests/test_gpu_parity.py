@@ -229,3 +229,41 @@ def test_attention_flags_data_errors():
                          float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
     assert int(st.item()) & sa.STATUS_UNION_LEN
+
+
+# ------------------------------------------------ residency stress and replayed selections
+@pytest.mark.parametrize("resident", [0.7, 0.05])
+def test_attention_partially_resident_pool_full_size(resident):
+    """The 32K chunk with a seeded share of its pages not resident (the page's
+    untested residency option), in the benchmark's launch configuration;
+    sampled groups against the oracle, rows without a resident cell output 0."""
+    w = synth.workload(2)
+    print("case resident", resident, flush=True)
+    d = synth.as_problem(synth.generate(w))
+    d["page_table"] = synth.drop_pages(d["page_table"], resident, seed=5)
+    out, cells, mask, length, status = H.run_path(d)
+    assert status == 0
+    H.assert_union_equal(cells, mask, length, oracle.union(d["sel"], d["sel_len"], w.n_ctx))
+    rows = H.sample_rows(w.n_q, 24, seed=4)
+    H.assert_close(out[rows], oracle.attention_of(d, rows=rows), "resident %.2f" % resident)
+    pt = d["page_table"]
+    for j in rows:
+        if not np.any(pt[d["sel"][j, :d["sel_len"][j]] // 64] >= 0):
+            assert np.all(out[j] == 0)
+
+
+def test_attention_replayed_selection_file(tmp_path):
+    """Selections written to a file and read back (the page's replay of a
+    selection dump); here the file holds the selection step's rows for
+    AR(1) block scores, replayed over the 8K workload's pools."""
+    from oracle import selection
+    w = synth.workload(1)
+    print("case replay", w.name, flush=True)
+    scores = synth.block_scores(w.n_q, w.n_ctx, 0.95, seed=21)
+    sel, sel_len = selection.select_blocks(scores, w.first_pos, w.n_ctx)
+    path = str(tmp_path / "dump.npz")
+    synth.save_selections(path, sel, sel_len, w.n_ctx, w.first_pos)
+    rec = synth.load_selections(path)
+    d = synth.as_problem(synth.generate(w, with_sel=False))
+    d["sel"], d["sel_len"] = rec["sel"], rec["sel_len"]
+    _check_problem(d, rows=H.sample_rows(w.n_q, 40, seed=6), what="replay " + w.name)

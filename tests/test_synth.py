@@ -117,3 +117,28 @@ def test_block_scores_recipe():
     assert abs(a.std() - 1.0) < 0.1
     t = synth.block_scores(50, 640, 0.0, seed=4, levels=3)
     assert set(np.unique(t).tolist()) <= {0.0, 1.0, 2.0}
+
+
+def test_selection_file_round_trip(tmp_path):
+    w = synth.workload(1)
+    d = synth.generate(w, with_q=False, with_pools=False)
+    path = str(tmp_path / "sel.npz")
+    synth.save_selections(path, d["sel"], d["sel_len"], w.n_ctx, w.first_pos)
+    rec = synth.load_selections(path)
+    assert np.array_equal(rec["sel"], d["sel"]) and np.array_equal(rec["sel_len"], d["sel_len"])
+    assert rec["n_ctx"] == w.n_ctx and rec["first_pos"] == w.first_pos
+    # a non-causal entry is refused
+    bad = d["sel"].copy()
+    bad[0, 0] = w.first_pos + 1
+    synth.save_selections(path, bad, d["sel_len"], w.n_ctx, w.first_pos)
+    with pytest.raises(ValueError):
+        synth.load_selections(path)
+
+
+def test_drop_pages_fraction_and_seed():
+    pt = np.random.default_rng(0).permutation(1000).astype(np.int32)
+    a = synth.drop_pages(pt, 0.7, seed=3)
+    b = synth.drop_pages(pt, 0.7, seed=3)
+    assert np.array_equal(a, b) and np.count_nonzero(a == -1) == 300
+    keep = a >= 0
+    assert np.array_equal(a[keep], pt[keep])
