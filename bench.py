@@ -43,7 +43,15 @@ FLOP_PER_CELL_ROW = 4 * 128    # QK^T and PV, per (union cell, row)
 SELECT_RHO = 0.99              # AR(1) correlation of the block scores across positions
 # the kernel each op's roofline and counter summary is about
 OP_KERNELS = {"path": ("sel_attn_prefill_kernel", "union_build_kernel"),
-              "select": ("select_blocks_kernel",)}
+              "select": ("select_blocks_kernel",),
+              "positions": ("prefill_positions_kernel",)}
+DEFAULT_WORKLOAD = {"path": "ctx32k_drift005", "select": "ctx32k_drift005",
+                    "positions": "ctx64k_independent"}
+# algorithmic bytes of the per-position kernel: per (position, KV head, listed
+# cell) its K and V rows and two scales; per listed cell of a position its
+# selection entry and page-table entry; q and out as for the path
+POS_CELL_BYTES = 128 + 128 + 4 + 4
+POS_ENTRY_BYTES = 4 + 4
 
 
 def parse():
@@ -51,9 +59,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ctx32k_drift005")
-    ap.add_argument("--op", choices=("path", "select"), default="path",
-                    help="path: union + attention (the default); select: the selection step")
+    ap.add_argument("--workload", default=None,
+                    help="default: ctx32k_drift005 (ctx64k_independent for --op positions)")
+    ap.add_argument("--op", choices=("path", "select", "positions"), default="path",
+                    help="path: union + attention (the default); select: the selection step; "
+                         "positions: the per-position attention (no union)")
     ap.add_argument("--sel", metavar="FILE",
                     help="replay recorded selections (.npz from synth.save_selections) instead of "
                          "the workload's own; n_ctx and n_q come from the file")
@@ -69,10 +79,18 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
+# the kernel sources behind each op's counters
+OP_SOURCES = {"path": ("union_build.hip", "sel_attn_prefill.hip"),
+              "select": ("select_blocks.hip",),
+              "positions": ("prefill_positions.hip",)}
+
+
+def source_hash(op: str = "path") -> str:
+    """Hash of the op's kernel sources and the shared argument header: counters
+    taken on other bytes are not used."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_top_selection_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(OP_SOURCES[op] + ("sel_attn_internal.h",)):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -93,7 +111,7 @@ def counter_traffic(workload_name: str, op: str = "path"):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(op):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -136,7 +154,7 @@ def summarize(d: str, workload: str, op: str = "path"):
     with open(os.path.join(ROOT, "profiles", stats_name), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    rec = {"workload": workload, "source_hash": source_hash(), "commands": commands[1:3],
+    rec = {"workload": workload, "source_hash": source_hash(op), "commands": commands[1:3],
            "copy_bytes": COPY_BYTES, "kernels": {}}
     for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
         rows = [r for r in _csv_rows(os.path.join(d, sub, "pmc_counter_collection.csv"))
@@ -169,7 +187,7 @@ def summarize(d: str, workload: str, op: str = "path"):
     lines.append("kernel sources: sha256 prefix %s (the benchmark uses these bytes only while it "
                  "matches)" % rec["source_hash"])
     extra = ("" if op == "path" else " --op " + op) + \
-        ("" if workload == "ctx32k_drift005" else " --workload " + workload)
+        ("" if workload == DEFAULT_WORKLOAD[op] else " --workload " + workload)
     lines.append("made by: bash profile.sh OUTDIR%s; python3 bench.py --summarize OUTDIR%s" % (
         extra, extra))
     with open(os.path.join(ROOT, "profiles", stats_name), "w") as f:
@@ -180,6 +198,8 @@ def summarize(d: str, workload: str, op: str = "path"):
 
 def main():
     args = parse()
+    if args.workload is None:
+        args.workload = DEFAULT_WORKLOAD[args.op]
     if args.summarize:
         summarize(args.summarize, args.workload, args.op)
         return
@@ -236,14 +256,24 @@ def main():
     scale = float(inp["softmax_scale"])
     stream = torch.cuda.current_stream(dev)
 
+    positions = args.op == "positions"
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        sa.sel_attn_build_union(dims, t["sel"], t["sel_len"], cells, mask, length, status, stream)
+        if not positions:
+            sa.sel_attn_build_union(dims, t["sel"], t["sel_len"], cells, mask, length, status,
+                                    stream)
         if ev is not None:
             ev[1].record(stream)
-        sa.sel_attn_prefill(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"],
-                            t["page_table"], cells, mask, length, scale, out, status, stream)
+        if positions:
+            sa.sel_attn_prefill_positions(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"],
+                                          t["v_scale"], t["page_table"], t["sel"], t["sel_len"],
+                                          scale, out, status, stream)
+        else:
+            sa.sel_attn_prefill(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"],
+                                t["v_scale"], t["page_table"], cells, mask, length, scale, out,
+                                status, stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -265,14 +295,21 @@ def main():
     prefill_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_per_step = wall / steps * 1e3
 
-    lens = length.cpu().numpy().astype(np.int64)
-    union_cells = int(lens.sum())
-    alg_bytes = union_cells * w.n_kv * UNION_CELL_BYTES + w.n_q * w.n_qh * ROW_BYTES
-    union_kv_bytes = union_cells * w.n_kv * UNION_KV_BYTES
-    flops = union_cells * w.n_kv * 96 * FLOP_PER_CELL_ROW
+    if positions:
+        # every (position, KV head) gathers its own resident cells
+        alg_bytes = resident_cells * (w.n_kv * POS_CELL_BYTES + POS_ENTRY_BYTES) + \
+            w.n_q * w.n_qh * ROW_BYTES
+        kv_bytes = resident_cells * w.n_kv * UNION_KV_BYTES
+        flops = q_head_cells * FLOP_PER_CELL_ROW
+    else:
+        lens = length.cpu().numpy().astype(np.int64)
+        union_cells = int(lens.sum())
+        alg_bytes = union_cells * w.n_kv * UNION_CELL_BYTES + w.n_q * w.n_qh * ROW_BYTES
+        kv_bytes = union_cells * w.n_kv * UNION_KV_BYTES
+        flops = union_cells * w.n_kv * 96 * FLOP_PER_CELL_ROW
     achieved = alg_bytes / (prefill_ms * 1e-3) / 1e9
     # the committed counters were taken on the workload's own inputs
-    traffic = None if (args.sel or args.kv_resident < 1.0) else counter_traffic(w.name)
+    traffic = None if (args.sel or args.kv_resident < 1.0) else counter_traffic(w.name, args.op)
 
     if args.profile:
         # plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
@@ -282,8 +319,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    kernel = "prefill_positions_kernel" if positions else "sel_attn_prefill_kernel"
     result = {
-        "metric": "selected query-head-cells/s (32K-context prompt chunk)",
+        "metric": ("selected query-head-cells/s (per-position attention, %s)" % w.name if positions
+                   else "selected query-head-cells/s (32K-context prompt chunk)"),
         "value": q_head_cells / (ms_per_step * 1e-3),
         "unit": "query-head-cells/s",
         "n_gpus": 1,
@@ -303,14 +342,13 @@ def main():
             "drift": w.drift, "parallelism": "single GPU",
         },
         "prompt_positions_per_s": w.n_q / (ms_per_step * 1e-3),
-        "kernels_ms": {"union_build": union_ms, "prefill": prefill_ms},
-        "union": {"cells": union_cells, "mean_per_group": union_cells / g,
-                  "ratio_to_mean_selection": (union_cells / g) / float(sel_len.mean())},
-        "union_kv_GBps": union_kv_bytes / (prefill_ms * 1e-3) / 1e9,
-        "union_kv_frac_of_hbm_peak": union_kv_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms": ({"prefill_positions": prefill_ms} if positions
+                       else {"union_build": union_ms, "prefill": prefill_ms}),
+        "kv_GBps": kv_bytes / (prefill_ms * 1e-3) / 1e9,
+        "kv_frac_of_hbm_peak": kv_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "mfma_frac_of_f16_peak": flops / (prefill_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS,
         "roofline": {
-            "kernel": "sel_attn_prefill_kernel",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
@@ -319,8 +357,11 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg_bytes,
         },
-        "source_hash": source_hash(),
+        "source_hash": source_hash(args.op),
     }
+    if not positions:
+        result["union"] = {"cells": union_cells, "mean_per_group": union_cells / g,
+                           "ratio_to_mean_selection": (union_cells / g) / float(sel_len.mean())}
 
     if args.cpu_rows != 0 and not args.profile:
         import oracle
@@ -435,7 +476,7 @@ def bench_select(args):
             "traffic": counter_traffic(w.name, "select"),
             "algorithmic_bytes_per_launch": alg_bytes,
         },
-        "source_hash": source_hash(),
+        "source_hash": source_hash("select"),
     }
     if args.cpu_rows != 0 and not args.profile:
         from oracle import selection as S

@@ -20,6 +20,9 @@
  *   sel_attn_prefill      union + q + paged INT8 K/V -> attention output
  * and the step before it, when the selections come from block scores:
  *   sel_attn_select_blocks  block scores -> per-position selections
+ * For batches whose neighbouring selections hardly overlap, one call does the
+ * same attention without a union:
+ *   sel_attn_prefill_positions  selections + q + paged INT8 K/V -> output
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -70,6 +73,7 @@ extern "C" {
 #define SEL_ATTN_TOP_BLOCKS 31     /* earlier blocks a selection takes by score */
 #define SEL_ATTN_SEL_MAX 2051      /* 3 + 31*64 + 64: cells in a full selection */
 #define SEL_ATTN_SELECT_MAX_CTX 262144 /* n_ctx limit of sel_attn_select_blocks */
+#define SEL_ATTN_POSITIONS_MAX_CAP 2560  /* sel_cap limit of sel_attn_prefill_positions */
 
 typedef struct sel_attn_dims {
   int32_t n_ctx;     /* logical context length in cells, >= 1; page_table has
@@ -184,6 +188,34 @@ int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_poo
                      const int32_t* page_table, const int32_t* union_cells,
                      const uint8_t* union_mask, const int32_t* union_len,
                      float softmax_scale, float* out, uint32_t* status, hipStream_t stream);
+
+/*
+ * sel_attn_prefill_positions - the same attention as sel_attn_build_union +
+ * sel_attn_prefill, computed per position with no union: every position
+ * gathers its own selected cells (section Summary: the FP32 kernel in which
+ * every position gathers its own ~2,051 cells defines what is computed;
+ * section Extra Notes: the union kernel pays only when neighbouring selections
+ * overlap, and with independent selections it is no faster). Pick this call
+ * when the union of 8 neighbours is several times one selection.
+ *
+ *   q, k_pool, v_pool, k_scale, v_scale, page_table, softmax_scale, out,
+ *   status      as for sel_attn_prefill
+ *   sel, sel_len as for sel_attn_build_union: any order, repeats count once
+ *   Precision: Q, K, V and P' = p * v_scale * 2^6 enter the products as FP16
+ *   (round to nearest even); scores, softmax and sums are FP32. Results agree
+ *   with sel_attn_prefill's to rounding, not bitwise; they depend on the order
+ *   of each row's entries only through rounding, and identical inputs give
+ *   bitwise-identical outputs.
+ *   Errors: CELL_RANGE (the cell is dropped), SEL_LEN (clamped), PAGE_RANGE
+ *   (treated as not resident), V_SCALE (|v_scale| >= 4: the cell's value
+ *   counts as 0). sel_cap > SEL_ATTN_POSITIONS_MAX_CAP gives EUNSUPPORTED.
+ *   Alignment: q, out, k_pool, v_pool 16 bytes; the rest 4 bytes.
+ */
+int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                               const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                               const int32_t* page_table, const int32_t* sel,
+                               const int32_t* sel_len, float softmax_scale, float* out,
+                               uint32_t* status, hipStream_t stream);
 
 /*
  * sel_attn_last_error - text describing the last nonzero return of an entry

@@ -7,10 +7,11 @@ fallback: importing this package fails loudly when libselattn.so is missing,
 and every call raises when the library returns an error code.
 
 The functions named like the C entry points (sel_attn_select_blocks,
-sel_attn_build_union, sel_attn_prefill, sel_attn_last_error) take preallocated
-device tensors and mirror include/sel_attn.h one to one. select_blocks(),
-build_union(), prefill() and check_status() are conveniences that allocate
-outputs and read the status word.
+sel_attn_build_union, sel_attn_prefill, sel_attn_prefill_positions,
+sel_attn_last_error) take preallocated device tensors and mirror
+include/sel_attn.h one to one. select_blocks(), build_union(), prefill(),
+prefill_positions() and check_status() are conveniences that allocate outputs
+and read the status word.
 
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
 (opt-in STRATA_PROMPT_ATTN_UNION=1)", section Summary.
@@ -51,9 +52,10 @@ SINKS = 3
 TOP_BLOCKS = 31
 SEL_MAX = 2051
 SELECT_MAX_CTX = 262144
+POSITIONS_MAX_CAP = 2560
 
 EXPORTED = ("sel_attn_select_blocks", "sel_attn_build_union", "sel_attn_prefill",
-            "sel_attn_last_error")
+            "sel_attn_prefill_positions", "sel_attn_last_error")
 
 
 class Dims(ctypes.Structure):
@@ -77,6 +79,9 @@ _lib.sel_attn_build_union.restype = ctypes.c_int
 _lib.sel_attn_prefill.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                   ctypes.c_float, _p, _p, _p]
 _lib.sel_attn_prefill.restype = ctypes.c_int
+_lib.sel_attn_prefill_positions.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
+                                            ctypes.c_float, _p, _p, _p]
+_lib.sel_attn_prefill_positions.restype = ctypes.c_int
 _lib.sel_attn_last_error.argtypes = []
 _lib.sel_attn_last_error.restype = ctypes.c_char_p
 
@@ -136,6 +141,16 @@ def sel_attn_prefill(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table
                                  _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
                                  ctypes.c_float(float(softmax_scale)), _ptr(out), _ptr(status),
                                  _stream(stream)))
+
+
+def sel_attn_prefill_positions(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel,
+                               sel_len, softmax_scale: float, out, status, stream=None) -> None:
+    """Enqueue the per-position attention (see include/sel_attn.h). Tensors or raw device pointers."""
+    _check(_lib.sel_attn_prefill_positions(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                           _ptr(k_scale), _ptr(v_scale), _ptr(page_table),
+                                           _ptr(sel), _ptr(sel_len),
+                                           ctypes.c_float(float(softmax_scale)), _ptr(out),
+                                           _ptr(status), _stream(stream)))
 
 
 # --------------------------------------------------------------------------
@@ -250,6 +265,39 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
     dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=cap, head_dim=hd, page_size=ps)
     sel_attn_prefill(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
                      union_mask, union_len, softmax_scale, out, status, stream)
+    return out, status
+
+
+def prefill_positions(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+                      softmax_scale: float, n_ctx: int, status=None, stream=None, out=None):
+    """Per-position attention over each position's own selection (no union).
+    Returns (out, status)."""
+    dev = q.device
+    _need(q, "q", torch.float32, 3, None)
+    for name, t, dt, nd in (("k_pool", k_pool, torch.int8, 4), ("v_pool", v_pool, torch.int8, 4),
+                            ("k_scale", k_scale, torch.float32, 3),
+                            ("v_scale", v_scale, torch.float32, 3),
+                            ("page_table", page_table, torch.int32, 1),
+                            ("sel", sel, torch.int32, 2), ("sel_len", sel_len, torch.int32, 1)):
+        _need(t, name, dt, nd, dev)
+    n_q, n_qh, hd = q.shape
+    n_pages, n_kv, ps, hd2 = k_pool.shape
+    if v_pool.shape != k_pool.shape or tuple(k_scale.shape) != (n_pages, n_kv, ps) or \
+            tuple(v_scale.shape) != (n_pages, n_kv, ps):
+        raise ValueError("pool / scale shapes disagree")
+    if hd2 != hd or n_qh != n_kv * Q_PER_KV:
+        raise ValueError("q is [n_q][n_kv*12][head_dim] with the pools' n_kv and head_dim")
+    if page_table.shape[0] < -(-n_ctx // ps):
+        raise ValueError("page_table needs ceil(n_ctx / page_size) entries")
+    if sel.shape[0] != n_q or sel_len.shape[0] != n_q:
+        raise ValueError("sel and sel_len must have n_q rows")
+    if out is None:
+        out = torch.empty_like(q)
+    if status is None:
+        status = new_status(dev)
+    dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=sel.shape[1], head_dim=hd, page_size=ps)
+    sel_attn_prefill_positions(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+                               softmax_scale, out, status, stream)
     return out, status
 
 

@@ -213,4 +213,55 @@ int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_poo
   return SEL_ATTN_OK;
 }
 
+int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                               const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                               const int32_t* page_table, const int32_t* sel,
+                               const int32_t* sel_len, float softmax_scale, float* out,
+                               uint32_t* status, hipStream_t stream) {
+  static const char* who = "sel_attn_prefill_positions";
+  int rc = check_dims(d, who);
+  if (rc) return rc;
+  if (!status) return fail(SEL_ATTN_EINVAL, "%s: status is NULL", who);
+  if (!isfinite(softmax_scale))
+    return fail(SEL_ATTN_EINVAL, "%s: softmax_scale must be finite", who);
+  if (d->sel_cap > SEL_ATTN_POSITIONS_MAX_CAP)
+    return fail(SEL_ATTN_EUNSUPPORTED, "%s: sel_cap %d above %d", who, d->sel_cap,
+                SEL_ATTN_POSITIONS_MAX_CAP);
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
+  if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !sel || !sel_len || !out)
+    return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(SEL_ATTN_EINVAL, "%s: q, out, k_pool and v_pool must be 16-byte aligned", who);
+  if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(page_table, 4) ||
+      !aligned(sel, 4) || !aligned(sel_len, 4) || !aligned(status, 4))
+    return fail(SEL_ATTN_EINVAL, "%s: scale and int32 arrays must be 4-byte aligned", who);
+  rc = check_device(who);
+  if (rc) return rc;
+  selattn::PositionsArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.page_table = page_table;
+  a.sel = sel;
+  a.sel_len = sel_len;
+  a.out = out;
+  a.status = status;
+  a.score_scale = softmax_scale * 1.4426950408889634f;
+  a.n_ctx = d->n_ctx;
+  a.n_q = d->n_q;
+  a.n_kv = d->n_kv;
+  a.n_pages = d->n_pages;
+  a.sel_cap = d->sel_cap;
+  a.per_xcd = (d->n_q + 7) / 8;
+  hipError_t e = selattn::launch_prefill_positions(a, stream);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SEL_ATTN_OK;
+}
+
 }  // extern "C"

@@ -52,7 +52,28 @@ struct SelectArgs {
   int32_t sel_cap;
 };
 
+struct PositionsArgs {
+  const float* q;
+  const int8_t* k_pool;
+  const int8_t* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* page_table;
+  const int32_t* sel;
+  const int32_t* sel_len;
+  float* out;
+  uint32_t* status;
+  float score_scale;   // softmax_scale * log2(e)
+  int32_t n_ctx;
+  int32_t n_q;
+  int32_t n_kv;
+  int32_t n_pages;
+  int32_t sel_cap;
+  int32_t per_xcd;     // positions each XCD walks through (grid = 8 * per_xcd)
+};
+
 hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t stream);
+hipError_t launch_prefill_positions(const PositionsArgs& a, hipStream_t stream);
 hipError_t launch_union_build(const UnionArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

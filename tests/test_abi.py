@@ -19,7 +19,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["sel_attn_build_union", "sel_attn_last_error",
-                                    "sel_attn_prefill", "sel_attn_select_blocks"]
+                                    "sel_attn_prefill", "sel_attn_prefill_positions",
+                                    "sel_attn_select_blocks"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -86,6 +87,28 @@ def test_select_blocks_rejects_on_host(kw, first, code):
         with pytest.raises(sa.SelAttnError) as e:
             sa.sel_attn_select_blocks(_dims(**kw), first - 1, FAKE, None, FAKE, stream=0)
         assert "NULL" in sa.sel_attn_last_error()
+
+
+def test_prefill_positions_rejects_on_host():
+    import sparse_top_selection_amd as sa
+    args = (FAKE,) * 8
+    with pytest.raises(sa.SelAttnError) as e:   # row stride over the supported cap
+        sa.sel_attn_prefill_positions(_dims(sel_cap=2561), *args, 0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -2 and "sel_attn_prefill_positions" in sa.sel_attn_last_error()
+    with pytest.raises(sa.SelAttnError) as e:   # q must be 16-byte aligned
+        sa.sel_attn_prefill_positions(_dims(), FAKE + 4, *args[1:], 0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:   # status is required
+        sa.sel_attn_prefill_positions(_dims(), *args, 0.1, FAKE, None, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:   # a NULL selection
+        sa.sel_attn_prefill_positions(_dims(), *args[:6], None, FAKE, 0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_prefill_positions(_dims(), *args, float("nan"), FAKE, FAKE, stream=0)
+    assert e.value.code == -1
+    sa.sel_attn_prefill_positions(_dims(n_q=0), *(None,) * 8, 0.1, None, FAKE, stream=0)
+    assert sa.sel_attn_last_error() == ""
 
 
 def test_null_and_misaligned_pointers_rejected_on_host():
