@@ -44,9 +44,10 @@ SELECT_RHO = 0.99              # AR(1) correlation of the block scores across po
 # the kernel each op's roofline and counter summary is about
 OP_KERNELS = {"path": ("sel_attn_prefill_kernel", "union_build_kernel"),
               "select": ("select_blocks_kernel",),
-              "positions": ("prefill_positions_kernel",)}
+              "positions": ("prefill_positions_kernel",),
+              "decode": ("decode_split_kernel", "decode_merge_kernel")}
 DEFAULT_WORKLOAD = {"path": "ctx32k_drift005", "select": "ctx32k_drift005",
-                    "positions": "ctx64k_independent"}
+                    "positions": "ctx64k_independent", "decode": "ctx64k_independent"}
 # algorithmic bytes of the per-position kernel: per (position, KV head, listed
 # cell) its K and V rows and two scales; per listed cell of a position its
 # selection entry and page-table entry; q and out as for the path
@@ -61,9 +62,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     help="default: ctx32k_drift005 (ctx64k_independent for --op positions)")
-    ap.add_argument("--op", choices=("path", "select", "positions"), default="path",
+    ap.add_argument("--op", choices=("path", "select", "positions", "decode"), default="path",
                     help="path: union + attention (the default); select: the selection step; "
-                         "positions: the per-position attention (no union)")
+                         "positions: the per-position attention (no union); decode: the last "
+                         "--decode-positions positions of the workload, split over their cells")
+    ap.add_argument("--decode-positions", type=int, default=1, metavar="N",
+                    help="positions per decode call (1 = decode, 5 = a verify window of 4 drafts)")
     ap.add_argument("--sel", metavar="FILE",
                     help="replay recorded selections (.npz from synth.save_selections) instead of "
                          "the workload's own; n_ctx and n_q come from the file")
@@ -82,7 +86,8 @@ def parse():
 # the kernel sources behind each op's counters
 OP_SOURCES = {"path": ("union_build.hip", "sel_attn_prefill.hip"),
               "select": ("select_blocks.hip",),
-              "positions": ("prefill_positions.hip",)}
+              "positions": ("prefill_positions.hip",),
+              "decode": ("prefill_positions.hip",)}
 
 
 def source_hash(op: str = "path") -> str:
@@ -217,6 +222,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.op == "select":
         bench_select(args)
+        return
+    if args.op == "decode":
+        bench_decode(args)
         return
     dev = torch.device("cuda:0")
     w = synth.workload(args.workload)
@@ -388,6 +396,105 @@ def main():
         }
         result["parity_on_cpu_sample"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
                                           "out_rms": float(np.sqrt(np.mean(ref ** 2)))}
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(args):
+    """The decode call on the workload's last N positions (its pools, q and
+    selections): one call per step, timed like the selection step (one event
+    pair around K back-to-back calls queued behind device copies)."""
+    import torch
+    import synth
+    import sparse_top_selection_amd as sa
+
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    nd = args.decode_positions
+    inp = synth.as_problem(synth.generate(w))
+    for k in ("q", "sel", "sel_len"):
+        inp[k] = np.ascontiguousarray(inp[k][-nd:])
+    inp["n_q"] = nd
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+         for k in ("q", "k_pool", "v_pool", "k_scale", "v_scale", "page_table", "sel", "sel_len")}
+    out = torch.empty_like(t["q"])
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dims = sa.make_dims(w.n_ctx, nd, w.n_kv, w.pool_pages, sel_cap=w.sel_cap)
+    ws_bytes = sa.sel_attn_decode_workspace_bytes(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    scale = float(inp["softmax_scale"])
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        sa.sel_attn_decode(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"],
+                           t["page_table"], t["sel"], t["sel_len"], scale, out, ws, ws_bytes,
+                           status, stream)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    sa.check_status(status)
+    steps = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not args.profile:
+        busy_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        busy_dst = torch.empty_like(busy_src)
+        torch.cuda.synchronize()
+        for _ in range(8 + steps // 4):   # ~0.2 ms each; enqueueing a call takes ~50 us
+            busy_dst.copy_(busy_src)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sa.check_status(status)
+    us = e0.elapsed_time(e1) / steps * 1e3
+
+    pt = inp["page_table"]
+    cells = 0
+    for j in range(nd):
+        row = np.unique(inp["sel"][j, :inp["sel_len"][j]])
+        cells += int(np.count_nonzero(pt[row // 64] >= 0))
+    alg_bytes = cells * (w.n_kv * POS_CELL_BYTES + POS_ENTRY_BYTES) + nd * w.n_qh * ROW_BYTES
+    achieved = alg_bytes / (us * 1e-6) / 1e9
+    if args.profile:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    result = {
+        "metric": "decode attention latency (%d position%s at the end of %s)" % (
+            nd, "" if nd == 1 else "s", w.name),
+        "value": us, "unit": "us", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": us * 1e-3, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8 K/V, fp16 products, fp32 softmax and sums",
+        "data": "synthetic (seeded; the workload's last positions)",
+        "config": {"workload": "decode%d_%s" % (nd, w.name), "n_ctx": w.n_ctx, "positions": nd,
+                   "kv_heads": w.n_kv, "cells": cells, "splits": (w.sel_cap + 63) // 64,
+                   "parallelism": "single GPU"},
+        "timing": "one HIP event pair around K back-to-back calls queued behind device copies",
+        "roofline": {"kernel": "decode_split_kernel + decode_merge_kernel", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "source_hash": source_hash("decode"),
+    }
+    if args.cpu_rows != 0 and not args.profile:
+        import oracle
+        cores = oracle.max_threads()
+        c0 = time.perf_counter()
+        reps = 0
+        while True:
+            ref = oracle.attention_of(inp, n_threads=cores)
+            reps += 1
+            if time.perf_counter() - c0 > 1.0:
+                break
+        cpu_s = (time.perf_counter() - c0) / reps
+        err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+        result["cpu_baseline"] = {"value": cpu_s * 1e6, "unit": "us", "cores": cores,
+                                  "kind": "oracle",
+                                  "sample": "the same %d position(s), FP64, %d repeats" % (nd, reps)}
+        result["parity_on_cpu_sample"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean())}
     print(json.dumps(result), flush=True)
 
 

@@ -23,6 +23,9 @@
  * For batches whose neighbouring selections hardly overlap, one call does the
  * same attention without a union:
  *   sel_attn_prefill_positions  selections + q + paged INT8 K/V -> output
+ * and for decode (one position, or a short speculative verify window), the
+ * same attention split over each position's cells:
+ *   sel_attn_decode             selections + q + paged INT8 K/V -> output
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -44,6 +47,7 @@
 #ifndef SEL_ATTN_H_
 #define SEL_ATTN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -73,7 +77,8 @@ extern "C" {
 #define SEL_ATTN_TOP_BLOCKS 31     /* earlier blocks a selection takes by score */
 #define SEL_ATTN_SEL_MAX 2051      /* 3 + 31*64 + 64: cells in a full selection */
 #define SEL_ATTN_SELECT_MAX_CTX 262144 /* n_ctx limit of sel_attn_select_blocks */
-#define SEL_ATTN_POSITIONS_MAX_CAP 2560  /* sel_cap limit of sel_attn_prefill_positions */
+#define SEL_ATTN_POSITIONS_MAX_CAP 2560  /* sel_cap limit of sel_attn_prefill_positions and decode */
+#define SEL_ATTN_DECODE_MAX_Q 65535      /* n_q limit of sel_attn_decode (one grid dimension) */
 
 typedef struct sel_attn_dims {
   int32_t n_ctx;     /* logical context length in cells, >= 1; page_table has
@@ -216,6 +221,39 @@ int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int
                                const int32_t* page_table, const int32_t* sel,
                                const int32_t* sel_len, float softmax_scale, float* out,
                                uint32_t* status, hipStream_t stream);
+
+/*
+ * sel_attn_decode_workspace_bytes - device workspace that sel_attn_decode needs
+ * for these dims: n_q * n_kv * ceil(sel_cap / 64) records of 6,272 bytes.
+ * Returns 0 when the dims are invalid (sel_attn_decode then says why).
+ */
+size_t sel_attn_decode_workspace_bytes(const sel_attn_dims* d);
+
+/*
+ * sel_attn_decode - the attention of sel_attn_prefill_positions for a few
+ * positions (decode, or a speculative verify window), each position's cells
+ * split into pieces of 64 so that one position occupies dozens of work-groups.
+ * The page leaves decode as it is (section Summary: decode tok/s and the verify
+ * window's time are unchanged); this is the same definition as the prompt path
+ * (section Summary: every position attends to exactly its own cells), for the
+ * decode workload.
+ *
+ *   arguments as for sel_attn_prefill_positions, plus
+ *   workspace        device memory of at least workspace_bytes =
+ *                    sel_attn_decode_workspace_bytes(d), 16-byte aligned,
+ *                    owned by the caller; overwritten by the call, so calls
+ *                    that run at the same time need workspaces of their own
+ *   Two kernels on `stream`: the splits, then their merge. Results agree with
+ *   sel_attn_prefill_positions to rounding; identical inputs give identical
+ *   bits. Meant for small n_q: every split repeats its position's dedup.
+ *   Errors: as sel_attn_prefill_positions; a workspace that is NULL, too small
+ *   or misaligned, or n_q > SEL_ATTN_DECODE_MAX_Q, gives EINVAL.
+ */
+int sel_attn_decode(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                    const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                    const int32_t* page_table, const int32_t* sel, const int32_t* sel_len,
+                    float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                    uint32_t* status, hipStream_t stream);
 
 /*
  * sel_attn_last_error - text describing the last nonzero return of an entry

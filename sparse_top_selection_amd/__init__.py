@@ -8,10 +8,10 @@ and every call raises when the library returns an error code.
 
 The functions named like the C entry points (sel_attn_select_blocks,
 sel_attn_build_union, sel_attn_prefill, sel_attn_prefill_positions,
-sel_attn_last_error) take preallocated device tensors and mirror
-include/sel_attn.h one to one. select_blocks(), build_union(), prefill(),
-prefill_positions() and check_status() are conveniences that allocate outputs
-and read the status word.
+sel_attn_decode, sel_attn_decode_workspace_bytes, sel_attn_last_error) take
+preallocated device tensors and mirror include/sel_attn.h one to one.
+select_blocks(), build_union(), prefill(), prefill_positions(), decode() and
+check_status() are conveniences that allocate outputs and read the status word.
 
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
 (opt-in STRATA_PROMPT_ATTN_UNION=1)", section Summary.
@@ -53,9 +53,11 @@ TOP_BLOCKS = 31
 SEL_MAX = 2051
 SELECT_MAX_CTX = 262144
 POSITIONS_MAX_CAP = 2560
+DECODE_MAX_Q = 65535
 
 EXPORTED = ("sel_attn_select_blocks", "sel_attn_build_union", "sel_attn_prefill",
-            "sel_attn_prefill_positions", "sel_attn_last_error")
+            "sel_attn_prefill_positions", "sel_attn_decode_workspace_bytes", "sel_attn_decode",
+            "sel_attn_last_error")
 
 
 class Dims(ctypes.Structure):
@@ -82,6 +84,11 @@ _lib.sel_attn_prefill.restype = ctypes.c_int
 _lib.sel_attn_prefill_positions.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
                                             ctypes.c_float, _p, _p, _p]
 _lib.sel_attn_prefill_positions.restype = ctypes.c_int
+_lib.sel_attn_decode_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+_lib.sel_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.sel_attn_decode.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
+                                 ctypes.c_float, _p, _p, ctypes.c_size_t, _p, _p]
+_lib.sel_attn_decode.restype = ctypes.c_int
 _lib.sel_attn_last_error.argtypes = []
 _lib.sel_attn_last_error.restype = ctypes.c_char_p
 
@@ -151,6 +158,22 @@ def sel_attn_prefill_positions(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, 
                                            _ptr(sel), _ptr(sel_len),
                                            ctypes.c_float(float(softmax_scale)), _ptr(out),
                                            _ptr(status), _stream(stream)))
+
+
+def sel_attn_decode_workspace_bytes(dims: Dims) -> int:
+    """Workspace bytes sel_attn_decode needs for these dims (0 if they are invalid)."""
+    return int(_lib.sel_attn_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+def sel_attn_decode(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+                    softmax_scale: float, out, workspace, workspace_bytes: int, status,
+                    stream=None) -> None:
+    """Enqueue the decode attention (see include/sel_attn.h). Tensors or raw device pointers."""
+    _check(_lib.sel_attn_decode(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(k_scale), _ptr(v_scale), _ptr(page_table), _ptr(sel),
+                                _ptr(sel_len), ctypes.c_float(float(softmax_scale)), _ptr(out),
+                                _ptr(workspace), int(workspace_bytes), _ptr(status),
+                                _stream(stream)))
 
 
 # --------------------------------------------------------------------------
@@ -268,10 +291,7 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
     return out, status
 
 
-def prefill_positions(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
-                      softmax_scale: float, n_ctx: int, status=None, stream=None, out=None):
-    """Per-position attention over each position's own selection (no union).
-    Returns (out, status)."""
+def _positions_dims(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, n_ctx):
     dev = q.device
     _need(q, "q", torch.float32, 3, None)
     for name, t, dt, nd in (("k_pool", k_pool, torch.int8, 4), ("v_pool", v_pool, torch.int8, 4),
@@ -291,13 +311,39 @@ def prefill_positions(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_
         raise ValueError("page_table needs ceil(n_ctx / page_size) entries")
     if sel.shape[0] != n_q or sel_len.shape[0] != n_q:
         raise ValueError("sel and sel_len must have n_q rows")
+    return make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=sel.shape[1], head_dim=hd, page_size=ps)
+
+
+def prefill_positions(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+                      softmax_scale: float, n_ctx: int, status=None, stream=None, out=None):
+    """Per-position attention over each position's own selection (no union).
+    Returns (out, status)."""
+    dims = _positions_dims(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, n_ctx)
     if out is None:
         out = torch.empty_like(q)
     if status is None:
-        status = new_status(dev)
-    dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=sel.shape[1], head_dim=hd, page_size=ps)
+        status = new_status(q.device)
     sel_attn_prefill_positions(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
                                softmax_scale, out, status, stream)
+    return out, status
+
+
+def decode(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, softmax_scale: float,
+           n_ctx: int, status=None, stream=None, out=None, workspace=None):
+    """Decode attention for a few positions, split over their cells. The
+    workspace (uint8 device tensor) is allocated when not given.
+    Returns (out, status)."""
+    dims = _positions_dims(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, n_ctx)
+    need = sel_attn_decode_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if status is None:
+        status = new_status(q.device)
+    sel_attn_decode(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+                    softmax_scale, out, workspace, workspace.numel() * workspace.element_size(),
+                    status, stream)
     return out, status
 
 

@@ -229,10 +229,12 @@ __device__ __forceinline__ void chunk_step(const PositionsArgs& a, const uint32_
   }
 }
 
-// Phase 2 for KV head h: 12 query rows over the n listed cells.
-__device__ __forceinline__ void attend_head(const PositionsArgs& a, const uint32_t* rows,
-                                            WaveTile& tile, int j, int h, int n, int lane,
-                                            uint32_t& flags) {
+// KV head h's 12 query rows over the n cells rows[0..n): the running state,
+// with the row's probability sum and sum(P') gathered over its four lanes.
+__device__ __forceinline__ void attend_range(const PositionsArgs& a, const uint32_t* rows,
+                                             WaveTile& tile, int j, int h, int n, int lane,
+                                             uint32_t& flags, ChunkState& st, float& l_row,
+                                             float& lp_row) {
   const int g = lane >> 4, i = lane & 15;
   const int n_qh = a.n_kv * kQPerKv;
   const bool row_ok = i < kQPerKv;
@@ -261,7 +263,6 @@ __device__ __forceinline__ void attend_head(const PositionsArgs& a, const uint32
   qsum += __shfl_xor(qsum, 32);
   const float s_init = -1152.f * qsum;
 
-  ChunkState st;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) st.o[mt] = float4v{0.f, 0.f, 0.f, 0.f};
   st.m_run = kNoMax;
@@ -284,35 +285,21 @@ __device__ __forceinline__ void attend_head(const PositionsArgs& a, const uint32
     if (c < nch) chunk_step(a, rows, tile, st, c, nch, n, h, lane, s_init, qb, r0, r2, flags);
     if (c + 1 < nch) chunk_step(a, rows, tile, st, c + 1, nch, n, h, lane, s_init, qb, r1, r0, flags);
   }
-
-  // out = (O^T - 1152 sum(P')) / (2^6 sum(p)) over the row's four lanes
-  float l_run = st.l_run, lp = st.lp;
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  lp += __shfl_xor(lp, 16);
-  lp += __shfl_xor(lp, 32);
-  const float corr = 1152.f * lp;
-  const float inv = l_run > 0.f ? (1.f / kVFold) / l_run : 0.f;
-  if (row_ok) {
-    float* orow = a.out + ((int64_t)j * n_qh + h * kQPerKv + i) * kD + 4 * g;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      *reinterpret_cast<float4v*>(orow + 16 * mt) = (st.o[mt] - corr) * inv;
-  }
+  l_row = st.l_run;
+  lp_row = st.lp;
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+  lp_row += __shfl_xor(lp_row, 16);
+  lp_row += __shfl_xor(lp_row, 32);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(PositionsArgs a) {
-  __shared__ Smem sm;
+// Phase 1 (the whole work-group): position j's list of pool rows in sm.rows,
+// repeats, cells out of range and non-resident pages dropped, in row order.
+// Returns the list's length.
+__device__ __forceinline__ int build_list(const PositionsArgs& a, Smem& sm, int j, int tid,
+                                          int lane, int wave, uint32_t& flags) {
   int32_t* hash_key = sm.u.hash.key;
   int32_t* hash_first = sm.u.hash.first;
-  const int b = blockIdx.x;
-  const int j = (b & 7) * a.per_xcd + (b >> 3);   // neighbouring positions on one XCD
-  if (j >= a.n_q) return;                          // whole work-groups
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t flags = 0;
-
   int L = a.sel_len[j];
   if (L < 0 || L > a.sel_cap) {
     flags |= SEL_ATTN_STATUS_SEL_LEN;
@@ -320,7 +307,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(Position
   }
   const int32_t* srow = a.sel + (int64_t)j * a.sel_cap;
 
-  // ---- phase 1: the position's list of pool rows
   for (int s = tid; s < kHashSlots; s += kThreads) {
     hash_key[s] = -1;
     hash_first[s] = 0x7fffffff;
@@ -354,23 +340,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(Position
     }
   }
   __syncthreads();
+  // each cell's first entry looks up its page; all lookups are issued before
+  // the first is used (one memory round trip, not one per round)
+  int32_t page[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = tid + kThreads * k;
+    const int32_t c = cell[k];
+    page[k] = -1;
+    if (e < L && c >= 0 && c < a.n_ctx) {
+      uint32_t s = hash_slot(c);
+      while (hash_key[s] != c) s = (s + 1) & (kHashSlots - 1);
+      if (hash_first[s] == e) page[k] = a.page_table[c >> 6];
+      else cell[k] = -1;                 // a repeat
+    }
+  }
   int base = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int e = tid + kThreads * k;
-    bool keep = false;
-    uint32_t row = 0;
     const int32_t c = cell[k];
-    if (e < L && c >= 0 && c < a.n_ctx) {
-      uint32_t s = hash_slot(c);
-      while (hash_key[s] != c) s = (s + 1) & (kHashSlots - 1);
-      if (hash_first[s] == e) {   // the cell's first entry
-        const int32_t page = a.page_table[c >> 6];
-        if (page >= a.n_pages || page < -1) flags |= SEL_ATTN_STATUS_PAGE_RANGE;
-        keep = page >= 0 && page < a.n_pages;
-        row = ((uint32_t)page * (uint32_t)a.n_kv) * 64u + (uint32_t)(c & 63);
-      }
-    }
+    const bool first = e < L && c >= 0 && c < a.n_ctx;
+    if (first && (page[k] >= a.n_pages || page[k] < -1)) flags |= SEL_ATTN_STATUS_PAGE_RANGE;
+    const bool keep = first && page[k] >= 0 && page[k] < a.n_pages;
+    const uint32_t row = ((uint32_t)page[k] * (uint32_t)a.n_kv) * 64u + (uint32_t)(c & 63);
     const uint64_t m = __ballot(keep);
     if (lane == 0) sm.wave_count[k & 1][wave] = __popcll(m);
     __syncthreads();
@@ -385,17 +378,132 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(Position
     base += total;
   }
   __syncthreads();   // the list is complete; the hash area becomes the waves' tiles
-  const int n = base;
+  return base;
+}
 
-  // ---- phase 2: wave w takes KV heads w, w + 4, ...
-  for (int h = wave; h < a.n_kv; h += kWaves) attend_head(a, sm.rows, sm.u.tile[wave], j, h, n, lane, flags);
+__global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(PositionsArgs a) {
+  __shared__ Smem sm;
+  const int b = blockIdx.x;
+  const int j = (b & 7) * a.per_xcd + (b >> 3);   // neighbouring positions on one XCD
+  if (j >= a.n_q) return;                          // whole work-groups
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t flags = 0;
+  const int n = build_list(a, sm, j, tid, lane, wave, flags);
+
+  // phase 2: wave w takes KV heads w, w + 4, ...;
+  // out = (O^T - 1152 sum(P')) / (2^6 sum(p))
+  const int g = lane >> 4, i = lane & 15;
+  const int n_qh = a.n_kv * kQPerKv;
+  for (int h = wave; h < a.n_kv; h += kWaves) {
+    ChunkState st;
+    float l_row, lp_row;
+    attend_range(a, sm.rows, sm.u.tile[wave], j, h, n, lane, flags, st, l_row, lp_row);
+    const float corr = 1152.f * lp_row;
+    const float inv = l_row > 0.f ? (1.f / kVFold) / l_row : 0.f;
+    if (i < kQPerKv) {
+      float* orow = a.out + ((int64_t)j * n_qh + h * kQPerKv + i) * kD + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<float4v*>(orow + 16 * mt) = (st.o[mt] - corr) * inv;
+    }
+  }
   if (flags) atomicOr(a.status, flags);
+}
+
+// ---------------------------------------------------------------------------
+// Decode: a few positions (one, or a speculative verify window), each split
+// over its cells so that the GPU has enough work-groups. Work-group (s, j)
+// builds position j's list (every split of a position builds the same list)
+// and attends to entries [64s, 64s + 64) of it for every KV head. It writes
+// the split's unnormalised state; a second kernel merges the splits of each
+// (position, head) in the usual way: weights exp2(m_s - max m), sums of those
+// times O_s and l_s, then O / l.
+
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(PositionsArgs a,
+                                                                  DecodePartial* part) {
+  __shared__ Smem sm;
+  const int s = blockIdx.x;
+  const int j = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t flags = 0;
+  const int n = build_list(a, sm, j, tid, lane, wave, flags);
+  const int first = kDecodeSplit * s;
+  const int n_s = max(0, min(kDecodeSplit, n - first));
+
+  const int g = lane >> 4, i = lane & 15;
+  for (int h = wave; h < a.n_kv; h += kWaves) {
+    ChunkState st;
+    float l_row, lp_row;
+    attend_range(a, sm.rows + min(first, n), sm.u.tile[wave], j, h, n_s, lane, flags, st, l_row,
+                 lp_row);
+    DecodePartial& p = part[((int64_t)j * a.n_kv + h) * a.n_splits + s];
+    if (i < kQPerKv) {
+      const float corr = 1152.f * lp_row;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<float4v*>(&p.o[i][16 * mt + 4 * g]) = st.o[mt] - corr;
+      if (g == 0) {
+        p.m[i] = st.m_run;
+        p.l[i] = l_row;
+      }
+    }
+  }
+  if (flags) atomicOr(a.status, flags);
+}
+
+// One work-group per (query row, KV head, position), one thread per dim.
+// Thread s of the first wave reads split s's m and l (at most 40 splits), the
+// wave reduces them, and the weights go through LDS; then every thread sums
+// its dim over the splits with the loads unrolled.
+__global__ __launch_bounds__(kD) void decode_merge_kernel(PositionsArgs a, const DecodePartial* part) {
+  __shared__ float wsh[64];
+  __shared__ float lsh;
+  const int r = blockIdx.x;
+  const int h = blockIdx.y;
+  const int j = blockIdx.z;
+  const int d = threadIdx.x;
+  const DecodePartial* p = part + ((int64_t)j * a.n_kv + h) * a.n_splits;
+  if (d < 64) {
+    const bool ok = d < a.n_splits;
+    const float ms = ok ? p[d].m[r] : kNoMax;
+    const float ls = ok ? p[d].l[r] : 0.f;
+    float m = ms;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float w = ok ? __builtin_amdgcn_exp2f(ms - m) : 0.f;
+    float l = w * ls;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    wsh[d] = w;
+    if (d == 0) lsh = l;
+  }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < a.n_splits; ++s) acc += wsh[s] * p[s].o[r][d];
+  const float l = lsh;
+  const int n_qh = a.n_kv * kQPerKv;
+  a.out[((int64_t)j * n_qh + h * kQPerKv + r) * kD + d] = l > 0.f ? acc * ((1.f / kVFold) / l) : 0.f;
 }
 
 }  // namespace
 
 hipError_t launch_prefill_positions(const PositionsArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(prefill_positions_kernel, dim3(8 * a.per_xcd), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const PositionsArgs& a, DecodePartial* part, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_split_kernel, dim3(a.n_splits, a.n_q), dim3(kThreads), 0, stream, a,
+                     part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(kQPerKv, a.n_kv, a.n_q), dim3(kD), 0, stream, a,
+                     (const DecodePartial*)part);
   return hipGetLastError();
 }
 

@@ -213,12 +213,15 @@ int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_poo
   return SEL_ATTN_OK;
 }
 
-int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
-                               const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                               const int32_t* page_table, const int32_t* sel,
-                               const int32_t* sel_len, float softmax_scale, float* out,
-                               uint32_t* status, hipStream_t stream) {
-  static const char* who = "sel_attn_prefill_positions";
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the per-position calls, and their kernel arguments.
+int positions_args(const sel_attn_dims* d, const char* who, const float* q, const int8_t* k_pool,
+                   const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                   const int32_t* page_table, const int32_t* sel, const int32_t* sel_len,
+                   float softmax_scale, float* out, uint32_t* status, selattn::PositionsArgs& a) {
   int rc = check_dims(d, who);
   if (rc) return rc;
   if (!status) return fail(SEL_ATTN_EINVAL, "%s: status is NULL", who);
@@ -227,10 +230,7 @@ int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int
   if (d->sel_cap > SEL_ATTN_POSITIONS_MAX_CAP)
     return fail(SEL_ATTN_EUNSUPPORTED, "%s: sel_cap %d above %d", who, d->sel_cap,
                 SEL_ATTN_POSITIONS_MAX_CAP);
-  if (d->n_q == 0) {
-    g_err[0] = 0;
-    return SEL_ATTN_OK;
-  }
+  if (d->n_q == 0) return SEL_ATTN_OK;
   if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !sel || !sel_len || !out)
     return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
@@ -240,7 +240,6 @@ int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int
     return fail(SEL_ATTN_EINVAL, "%s: scale and int32 arrays must be 4-byte aligned", who);
   rc = check_device(who);
   if (rc) return rc;
-  selattn::PositionsArgs a;
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -258,7 +257,69 @@ int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int
   a.n_pages = d->n_pages;
   a.sel_cap = d->sel_cap;
   a.per_xcd = (d->n_q + 7) / 8;
+  a.n_splits = (d->sel_cap + selattn::kDecodeSplit - 1) / selattn::kDecodeSplit;
+  return SEL_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sel_attn_prefill_positions(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                               const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                               const int32_t* page_table, const int32_t* sel,
+                               const int32_t* sel_len, float softmax_scale, float* out,
+                               uint32_t* status, hipStream_t stream) {
+  static const char* who = "sel_attn_prefill_positions";
+  selattn::PositionsArgs a;
+  const int rc = positions_args(d, who, q, k_pool, v_pool, k_scale, v_scale, page_table, sel,
+                                sel_len, softmax_scale, out, status, a);
+  if (rc) return rc;
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
   hipError_t e = selattn::launch_prefill_positions(a, stream);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SEL_ATTN_OK;
+}
+
+size_t sel_attn_decode_workspace_bytes(const sel_attn_dims* d) {
+  if (check_dims(d, "sel_attn_decode_workspace_bytes")) return 0;
+  const size_t splits = (size_t)(d->sel_cap + selattn::kDecodeSplit - 1) / selattn::kDecodeSplit;
+  return (size_t)d->n_q * (size_t)d->n_kv * splits * sizeof(selattn::DecodePartial);
+}
+
+int sel_attn_decode(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                    const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                    const int32_t* page_table, const int32_t* sel, const int32_t* sel_len,
+                    float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                    uint32_t* status, hipStream_t stream) {
+  static const char* who = "sel_attn_decode";
+  // every check that needs no device comes before the device check
+  int rc = check_dims(d, who);
+  if (rc) return rc;
+  if (d->n_q > 0) {
+    const size_t need = sel_attn_decode_workspace_bytes(d);
+    if (!workspace || workspace_bytes < need)
+      return fail(SEL_ATTN_EINVAL, "%s: workspace of %zu bytes needed (got %zu%s)", who, need,
+                  workspace_bytes, workspace ? "" : ", NULL");
+    if (!aligned(workspace, 16))
+      return fail(SEL_ATTN_EINVAL, "%s: workspace must be 16-byte aligned", who);
+    if (d->n_q > SEL_ATTN_DECODE_MAX_Q)
+      return fail(SEL_ATTN_EINVAL, "%s: n_q %d above %d (the call is meant for a few positions)",
+                  who, d->n_q, SEL_ATTN_DECODE_MAX_Q);
+  }
+  selattn::PositionsArgs a;
+  rc = positions_args(d, who, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+                      softmax_scale, out, status, a);
+  if (rc) return rc;
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
+  hipError_t e = selattn::launch_decode(a, static_cast<selattn::DecodePartial*>(workspace), stream);
   if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
   g_err[0] = 0;
   return SEL_ATTN_OK;

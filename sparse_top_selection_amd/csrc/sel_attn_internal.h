@@ -70,10 +70,22 @@ struct PositionsArgs {
   int32_t n_pages;
   int32_t sel_cap;
   int32_t per_xcd;     // positions each XCD walks through (grid = 8 * per_xcd)
+  int32_t n_splits;    // decode: splits of each position's list (of kDecodeSplit cells)
+};
+
+// Decode: cells per split, and one split's unnormalised state for one
+// (position, KV head): running maximum (log2 domain), probability sum and
+// O (2^6 times sum p v, the V bias removed) of the 12 query rows.
+constexpr int kDecodeSplit = 64;   // at most 40 splits (sel_cap <= 2560)
+struct DecodePartial {
+  float m[16];
+  float l[16];
+  float o[12][128];
 };
 
 hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_prefill_positions(const PositionsArgs& a, hipStream_t stream);
+hipError_t launch_decode(const PositionsArgs& a, DecodePartial* part, hipStream_t stream);
 hipError_t launch_union_build(const UnionArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

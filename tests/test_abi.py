@@ -18,7 +18,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["sel_attn_build_union", "sel_attn_last_error",
+    assert declared_functions() == ["sel_attn_build_union", "sel_attn_decode",
+                                    "sel_attn_decode_workspace_bytes", "sel_attn_last_error",
                                     "sel_attn_prefill", "sel_attn_prefill_positions",
                                     "sel_attn_select_blocks"]
 
@@ -108,6 +109,28 @@ def test_prefill_positions_rejects_on_host():
         sa.sel_attn_prefill_positions(_dims(), *args, float("nan"), FAKE, FAKE, stream=0)
     assert e.value.code == -1
     sa.sel_attn_prefill_positions(_dims(n_q=0), *(None,) * 8, 0.1, None, FAKE, stream=0)
+    assert sa.sel_attn_last_error() == ""
+
+
+def test_decode_rejects_on_host():
+    import sparse_top_selection_amd as sa
+    d = _dims(n_q=3)
+    need = sa.sel_attn_decode_workspace_bytes(d)
+    assert need == 3 * 2 * 33 * 6272
+    args = (FAKE,) * 8
+    for ws, nbytes in ((None, need), (FAKE, need - 1), (FAKE + 8, need)):
+        with pytest.raises(sa.SelAttnError) as e:
+            sa.sel_attn_decode(d, *args, 0.1, FAKE, ws, nbytes, FAKE, stream=0)
+        assert e.value.code == -1 and "workspace" in sa.sel_attn_last_error()
+    with pytest.raises(sa.SelAttnError) as e:   # many positions: not a decode call
+        big = _dims(n_q=70000)
+        sa.sel_attn_decode(big, *args, 0.1, FAKE, FAKE, sa.sel_attn_decode_workspace_bytes(big),
+                           FAKE, stream=0)
+    assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_decode(_dims(sel_cap=2561), *args, 0.1, FAKE, FAKE, 1 << 30, FAKE, stream=0)
+    assert e.value.code == -2
+    sa.sel_attn_decode(_dims(n_q=0), *(None,) * 8, 0.1, None, None, 0, FAKE, stream=0)
     assert sa.sel_attn_last_error() == ""
 
 
