@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_PKG, "libselattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libselattn.so is not built (%s); run `python -m sparse_top_selection_amd.build`" % LIB_PATH)
+        "libselattn.so is not built (%s); run `python sparse_top_selection_amd/build.py`" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
 

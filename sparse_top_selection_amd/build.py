@@ -1,7 +1,8 @@
 """Build libselattn.so (HIP, gfx950) in-tree with hipcc.
 
-Run as `python -m sparse_top_selection_amd.build`. The library is rebuilt on
-every call to build(); the loader in __init__ never builds.
+Run as `python sparse_top_selection_amd/build.py` (a plain script: importing the
+package needs the library it builds). The library is rebuilt on every call to
+build(); the loader in __init__ never builds.
 """
 from __future__ import annotations
 

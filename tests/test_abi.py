@@ -165,3 +165,15 @@ def test_empty_query_batch_is_a_no_op():
     assert sa.sel_attn_last_error() == ""
     with pytest.raises(sa.SelAttnError):   # misaligned scores
         sa.sel_attn_select_blocks(_dims(sel_cap=2051), 0, FAKE + 2, FAKE, FAKE, stream=0)
+
+
+def test_builder_loads_without_the_library():
+    # A fresh checkout has no libselattn.so; the build step must still load
+    # its builder (the package itself refuses to import until it is built).
+    import subprocess
+    import sys
+    code = ("import sys, __graft_entry__ as g; m = g._load_builder(); "
+            "assert 'sparse_top_selection_amd' not in sys.modules; "
+            "assert m.sources(), 'no HIP sources'")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
