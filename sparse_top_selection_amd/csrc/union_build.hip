@@ -7,33 +7,42 @@
 // work-group per 8 positions, local bitmaps); section Extra Notes (a cell is an
 // int32, its mask a separate byte, so any context length works).
 //
-// gfx950 design: one 512-thread workgroup per group. The group's cells are
-// scattered into an LDS bitmap that holds one chooser byte per cell (4 cells per
-// 32-bit word, ds_or atomics), 32K cells per window (four workgroups fit a CU);
-// longer contexts take several windows in ascending order. When the rows fit
-// one pass of loads (2,560 entries each) they are read once into registers and
-// every window scatters from there. Compaction is one pass: thread t owns a contiguous
-// run of words, counts its nonzero bytes, a workgroup prefix sum (wave64 shuffles
-// plus one LDS exchange) gives its output offset, and it writes its cells in
-// ascending order. The bitmap is padded by one word per 32 so that 64 threads
-// reading word i of their runs fall on 64 distinct banks. Output order is
-// therefore ascending cell index, and the result is independent of row order and
-// repeats.
+// gfx950 design: one 512-thread workgroup per group, four per CU (32 KiB of LDS
+// and at most 64 VGPRs each), so that the 1,024 groups of an 8,192-position
+// chunk are all resident at once and the kernel is one round of workgroups.
+//   * The group's 8 selection rows are one contiguous span of 8 * sel_cap
+//     int32. It is read with 16-byte loads of the aligned 16-byte blocks that
+//     overlap it (a block holding one byte of the span lies in a mapped page),
+//     in batches of four per thread whose loads are all issued before the first
+//     is used; entries outside the span or past their row's length are skipped.
+//   * Every counted entry ORs bit i (its row) into the chooser byte of its cell
+//     in an LDS bitmap of one byte per cell, 32K cells per window (ds_or
+//     atomics); longer contexts take several windows in ascending order, each
+//     reading the span again (from cache).
+//   * Compaction walks the window in cell order: wave w owns an eighth of it.
+//     One pass of word reads counts its nonzero bytes and marks its nonempty
+//     256-cell slabs; an eight-entry prefix over the waves gives its output
+//     offset; then each nonempty slab is emitted 64 cells at a time (byte
+//     reads, ballot, mbcnt), so that consecutive lanes store consecutive union
+//     entries.
+// Output order is ascending cell index, and the result is independent of row
+// order and repeats.
 
 #include "sel_attn_internal.h"
 
 namespace selattn {
 namespace {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kWindowCells = 32768;                       // one chooser byte per cell
-constexpr int kWindowWords = kWindowCells / 4;
-constexpr int kPaddedWords = kWindowWords + kWindowWords / 32;   // 33 KiB of LDS
-constexpr int kPer = 5;                                   // entries per thread, row and pass
-
-// word w of the window lives at w + w / 32
-__device__ __forceinline__ int padded(int w) { return w + (w >> 5); }
+constexpr int kWindowCells = 32768;                 // one chooser byte per cell
+constexpr int kWindowWords = kWindowCells / 4;       // 32 KiB of LDS
+constexpr int kWaveWords = kWindowWords / kWaves;    // compaction share of a wave
+constexpr int kBatch = 4;                            // 16-byte loads per thread in flight
+constexpr int kSlabs = kWaveWords / 64;              // 256-cell slabs per wave (16)
 
 // number of nonzero bytes of x
 __device__ __forceinline__ int nonzero_bytes(uint32_t x) {
@@ -41,126 +50,185 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t x) {
   return __builtin_popcount(hi & 0x80808080u);
 }
 
-__global__ __launch_bounds__(kThreads) void union_build_kernel(UnionArgs a) {
-  __shared__ uint32_t bitmap[kPaddedWords];
-  __shared__ int wave_sum[2][kWaves];
+// 16-byte block b of the span's aligned cover (b < n_blocks; others read block 0)
+__device__ __forceinline__ i32x4 load_block(const int32_t* base, int b, int n_blocks) {
+  return *reinterpret_cast<const i32x4*>(base + 4 * (b < n_blocks ? b : 0));
+}
+
+// The rows of a block's four entries (f0 = flat index of entry 0 in the
+// span): byte j = row of entry j, or 0xff when the entry does not count
+// (outside the span, past its row's length, or a cell outside [0, n_ctx):
+// flagged).
+__device__ __forceinline__ uint32_t classify_block(const i32x4 x, int f0, int cap, float inv_cap,
+                                                   const int* row_end, int n_ctx, uint32_t& flags) {
+  const int vals[4] = {x.x, x.y, x.z, x.w};
+  uint32_t rw = 0xffffffffu;
+  if (cap >= 4) {
+    // rows of at least 4 entries: a block crosses at most one row end. Row of
+    // entry max(f0, 0): a float estimate, corrected to the exact one.
+    const int fc = max(f0, 0);
+    int row = min((int)((float)fc * inv_cap), 7);
+    if (row * cap > fc) --row;
+    if ((row + 1) * cap <= fc) ++row;
+    const int next = (row + 1) * cap;   // first entry of the next row
+    const int end0 = row_end[row];
+    const int end1 = row_end[min(row + 1, 7)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = f0 + j;
+      const bool second = f >= next;
+      const bool counts = f >= 0 && f < (second ? end1 : end0);
+      const bool in_ctx = (unsigned)vals[j] < (unsigned)n_ctx;
+      flags |= (counts && !in_ctx) ? SEL_ATTN_STATUS_CELL_RANGE : 0u;
+      const uint32_t r = (uint32_t)(second ? row + 1 : row);
+      if (counts && in_ctx) rw = (rw & ~(0xffu << (8 * j))) | (r << (8 * j));
+    }
+  } else {
+    // shorter rows: each entry's row by division
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = f0 + j;
+      if (f < 0 || f >= 8 * cap) continue;
+      const int r = f / cap;
+      if (f >= row_end[r]) continue;
+      if ((unsigned)vals[j] >= (unsigned)n_ctx) {
+        flags |= SEL_ATTN_STATUS_CELL_RANGE;
+        continue;
+      }
+      rw = (rw & ~(0xffu << (8 * j))) | ((uint32_t)r << (8 * j));
+    }
+  }
+  return rw;
+}
+
+// OR bit r into the chooser byte of every counted entry's cell in this window
+__device__ __forceinline__ void scatter_block(uint32_t* bitmap, const i32x4 x, uint32_t rw, int w0,
+                                              int win) {
+  const int vals[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t r = (rw >> (8 * j)) & 0xffu;
+    const unsigned rel = (unsigned)(vals[j] - w0);
+    if (r != 0xffu && rel < (unsigned)win) atomicOr(&bitmap[rel >> 2], (1u << r) << ((rel & 3u) * 8u));
+  }
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+__global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
+  __shared__ uint32_t bitmap[kWindowWords];
+  __shared__ int wave_cnt[2][kWaves];
+  __shared__ int row_end[8];   // flat index (within the span) past row i's entries
 
   const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n_pos = min(8, a.n_q - 8 * g);
-  const int64_t ucap = 8LL * a.sel_cap;
+  const int cap = a.sel_cap;
+  const int64_t ucap = 8LL * cap;
   int32_t* out_cells = a.union_cells + (int64_t)g * ucap;
   uint8_t* out_mask = a.union_mask + (int64_t)g * ucap;
 
   uint32_t flags = 0;
-  int len[8];
-  int max_len = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  if (tid < 8) {
     int L = 0;
-    if (i < n_pos) {
-      L = a.sel_len[8 * g + i];
-      if (L < 0 || L > a.sel_cap) {
+    if (tid < n_pos) {
+      L = a.sel_len[8 * g + tid];
+      if (L < 0 || L > cap) {
         flags |= SEL_ATTN_STATUS_SEL_LEN;
-        L = L < 0 ? 0 : a.sel_cap;
+        L = L < 0 ? 0 : cap;
       }
     }
-    len[i] = L;
-    max_len = max(max_len, L);
+    row_end[tid] = tid * cap + L;
   }
 
-  int32_t v[8][kPer];
-  auto load_pass = [&](int base) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int32_t* row = a.sel + (int64_t)(8 * g + (i < n_pos ? i : 0)) * a.sel_cap;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int e = base + tid + kThreads * k;
-        v[i][k] = (i < n_pos && e < len[i]) ? row[e] : -1;
-      }
-    }
-  };
-  auto scatter_pass = [&](int base, int w0, int win) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int e = base + tid + kThreads * k;
-        if (i >= n_pos || e >= len[i]) continue;
-        const int c = v[i][k];
-        if (c < 0 || c >= a.n_ctx) {
-          flags |= SEL_ATTN_STATUS_CELL_RANGE;
-          continue;
-        }
-        const unsigned r = (unsigned)(c - w0);
-        if (r < (unsigned)win) atomicOr(&bitmap[padded(r >> 2)], (1u << i) << ((r & 3u) * 8u));
-      }
-    }
-  };
-  const bool one_pass = max_len <= kThreads * kPer;
-  if (one_pass) load_pass(0);
+  // the span: n_pos rows from sel + 8g * cap, read as the aligned 16-byte
+  // blocks that overlap it; flat index f of a loaded entry = 4 * block - shift
+  const int32_t* span = a.sel + (int64_t)8 * g * cap;
+  const int shift = (int)((reinterpret_cast<uintptr_t>(span) >> 2) & 3u);
+  const int32_t* base = span - shift;
+  const int span_len = n_pos * cap;
+  const float inv_cap = 1.f / (float)cap;
+
+  // blocks of the span's aligned 16-byte cover
+  const int n_blocks = (int)(((int64_t)span_len + shift + 3) / 4);
+  __syncthreads();   // row_end
 
   int written = 0;  // union cells emitted so far (same value in every thread)
   int round = 0;
   for (int w0 = 0; w0 < a.n_ctx; w0 += kWindowCells, ++round) {
     const int win = min(kWindowCells, a.n_ctx - w0);
-    const int words = (win + 3) >> 2;
-    const int pwords = padded(words - 1) + 1;
-    for (int i = tid; i < pwords; i += kThreads) bitmap[i] = 0u;
+    // the first batch's loads go out before the bitmap is cleared
+    for (int i = tid; i < kWindowWords / 4; i += kThreads)
+      reinterpret_cast<u32x4*>(bitmap)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
 
-    // scatter: OR bit i into the byte of every cell row i selected. Entries are
-    // read in passes of kPer per thread and row, all loads of a pass issued
-    // before its atomics (one memory round trip per pass); with a single pass
-    // the registers are filled once, before the first window.
-    if (!one_pass) {
-      for (int base = 0; base < max_len; base += kThreads * kPer) {
-        load_pass(base);
-        scatter_pass(base, w0, win);
-      }
-    } else {
-      scatter_pass(0, w0, win);
-    }
-    __syncthreads();
-
-    // compaction: thread tid owns words [b0, b1)
-    const int per = (words + kThreads - 1) / kThreads;
-    const int b0 = min(tid * per, words);
-    const int b1 = min(b0 + per, words);
-    int cnt = 0;
-    for (int w = b0; w < b1; ++w) cnt += nonzero_bytes(bitmap[padded(w)]);
-    // inclusive prefix over the wave, then over the waves
-    int incl = cnt;
+    // scatter: the span in batches of kBatch blocks per thread, all loads of a
+    // batch issued before the first is used (one memory round trip per batch;
+    // later windows find the span in cache)
+    for (int b0 = 0; b0 < n_blocks; b0 += kThreads * kBatch) {
+      i32x4 raw[kBatch];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
+      for (int k = 0; k < kBatch; ++k) raw[k] = load_block(base, b0 + tid + kThreads * k, n_blocks);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int b = b0 + tid + kThreads * k;
+        if (b < n_blocks)
+          scatter_block(bitmap, raw[k],
+                        classify_block(raw[k], 4 * b - shift, cap, inv_cap, row_end, a.n_ctx, flags),
+                        w0, win);
+      }
     }
-    if (lane == 63) wave_sum[round & 1][wave] = incl;
     __syncthreads();
-    int before = 0, total = 0;
+
+    // compaction of this wave's share of the window: words
+    // [wave * kWaveWords, +kWaveWords), slabs of 64 words (256 cells). One
+    // pass of word reads counts the nonzero bytes and marks the nonempty slabs.
+    const int words = (win + 3) >> 2;
+    const int wb = wave * kWaveWords;
+    int cnt = 0;
+    uint32_t nonempty = 0;   // bit s: slab s holds a union cell (same in every lane)
+#pragma unroll
+    for (int s = 0; s < kSlabs; ++s) {
+      const uint32_t x = (wb + 64 * s < words) ? bitmap[wb + 64 * s + lane] : 0u;
+      cnt += nonzero_bytes(x);
+      nonempty |= __ballot(x != 0u) ? (1u << s) : 0u;
+    }
+    cnt = wave_sum(cnt);
+    if (lane == 0) wave_cnt[round & 1][wave] = cnt;
+    __syncthreads();
+    int o = written, total = 0;
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
-      const int t = wave_sum[round & 1][k];
-      before += (k < wave) ? t : 0;
+      const int t = wave_cnt[round & 1][k];
+      o += (k < wave) ? t : 0;
       total += t;
     }
-    int o = written + before + incl - cnt;
-    for (int w = b0; w < b1; ++w) {
-      const uint32_t x = bitmap[padded(w)];
-      if (x == 0u) continue;
-      const int cell0 = w0 + 4 * w;
+    // emission: nonempty slabs in order, 64 cells at a time, so that
+    // consecutive lanes store consecutive union entries
+    const uint8_t* bytes = reinterpret_cast<const uint8_t*>(bitmap);
+    while (nonempty) {
+      const int s = __builtin_ctz(nonempty);
+      nonempty &= nonempty - 1;
+      const int rel0 = 4 * (wb + 64 * s) + lane;   // cell within the window, k = 0
+      uint32_t m[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m[k] = bytes[rel0 + 64 * k];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t m = (x >> (8 * k)) & 0xffu;
-        if (m) {
-          out_cells[o] = cell0 + k;
-          out_mask[o] = (uint8_t)m;
-          ++o;
+        const uint64_t b = __ballot(m[k] != 0u);
+        if (m[k]) {
+          const int at = o + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+          out_cells[at] = w0 + rel0 + 64 * k;
+          out_mask[at] = (uint8_t)m[k];
         }
+        o += __builtin_popcountll(b);
       }
     }
     written += total;

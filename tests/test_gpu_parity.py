@@ -73,6 +73,32 @@ def test_union_bit_exact_edge_cases(n_ctx, n_q, seed):
                          oracle.union(sel, sel_len, n_ctx))
 
 
+@pytest.mark.parametrize("n_ctx,n_q,cap,offset,seed", [(100, 11, 13, 1, 7), (40000, 20, 5003, 3, 8),
+                                                        (9000, 16, 3, 2, 9), (2000, 9, 1, 1, 10),
+                                                        (70000, 24, 2051, 1, 11)])
+def test_union_bit_exact_any_row_stride_and_alignment(n_ctx, n_q, cap, offset, seed):
+    """Row strides that put groups at every 4-byte alignment, rows shorter than
+    a 16-byte block, and groups too long for one pass of loads."""
+    print("case", n_ctx, n_q, cap, offset, seed, flush=True)
+    rng = np.random.default_rng(seed)
+    sel = np.full((n_q, cap), -7, np.int32)
+    sel_len = rng.integers(0, cap + 1, size=n_q).astype(np.int32)
+    sel_len[0] = cap
+    for j in range(n_q):
+        sel[j, :sel_len[j]] = rng.integers(0, n_ctx, size=sel_len[j])
+    # the rows start `offset` int32 into a device buffer, so the sel pointer is
+    # only 4-byte aligned
+    flat = torch.full((offset + n_q * cap + 5,), -3, dtype=torch.int32)
+    flat[offset:offset + n_q * cap] = torch.from_numpy(sel.reshape(-1))
+    dev = flat.cuda()[offset:offset + n_q * cap].view(n_q, cap)
+    assert dev.data_ptr() % 16 != 0
+    cells, mask, length, status = sa.build_union(dev, torch.from_numpy(sel_len).cuda(), n_ctx)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
+                         oracle.union(sel, sel_len, n_ctx))
+
+
 def test_union_flags_bad_cells_and_lengths():
     sel = np.full((10, 16), -1, np.int32)
     sel_len = np.full(10, 3, np.int32)
