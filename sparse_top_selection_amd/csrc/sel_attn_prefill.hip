@@ -27,7 +27,8 @@
 //     and every cell of each chunk, with its own softmax state;
 //   * S^T (32 cells x 32 rows, K=128) is 8 v_mfma_f32_32x32x16_f16 from the K
 //     tile (LDS) and the wave's Q rows (FP16, held in registers for the whole
-//     work-group), after one MFMA that adds the K offset's term; O^T (128 dims x 32 rows)
+//     work-group); the first takes as its accumulator input a register set
+//     that holds the K offset's term of each row; O^T (128 dims x 32 rows)
 //     += V^T P'^T is 8 more MFMAs whose B operand (P'^T) comes straight from
 //     the S^T accumulator registers, and whose A operand is read transposed
 //     from the [cell][dim] V tile (ds_read_b64_tr_b16) in the same cell order;
@@ -35,8 +36,8 @@
 //     S^T(c+1) chain with the softmax of chunk c between its MFMAs, so the
 //     matrix pipe and the VALU work at the same time;
 //   * K and V integers (plus the +1152 offset of the byte-to-FP16 trick) are
-//     exact in FP16; the K offset is removed by starting each S^T chain with
-//     -1152 sum(Q) of its row, k_scale * softmax_scale * log2(e) multiplies
+//     exact in FP16; the K offset is removed by starting each S^T chain from
+//     -1152 sum(Q) of its row (FP32, kept in registers), k_scale * softmax_scale * log2(e) multiplies
 //     the score in FP32, and the FP16 probabilities are multiplied by the FP16
 //     v factor v_scale * 2^6 (2^-6 returns in the epilogue). Each lane tracks
 //     the sum of the P' values it feeds the MFMA; 1152 times that sum (the V
@@ -276,23 +277,17 @@ __device__ __forceinline__ void finish_translation(const PrefillArgs& a, const P
 
 // ---------------------------------------------------------------------------
 // Consumer waves 0..2: row block w (32 rows).
-// The K tile holds k + 1152, so every S^T chain starts with an MFMA that adds
-// -1152 sum(Q) of each row: A has ones in k-slots 0 and 1 (lanes of half 0),
-// B the row's value split into two FP16 terms there (hi + lo, exact to FP32
-// precision), all other slots zero.
-__device__ __forceinline__ float16v offset_start(const half8& ones9, const half8& q9) {
-  float16v z;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) z[r] = 0.f;
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(ones9, q9, z, 0, 0, 0);
-}
+// The K tile holds k + 1152, so every S^T chain starts from -1152 sum(Q) of
+// each row instead of zero: the first MFMA reads it as its accumulator input
+// from a register set filled once per work-group (the value is the same for
+// all 16 accumulator entries of a lane, which share the lane's row).
 
 // S^T (the chunk's 32 cells x this wave's 32 rows). q: this lane's Q operands
 // (k-step ks: dims 16ks + 8hb .. +7 of its row), in registers for the whole
 // work-group.
-__device__ __forceinline__ float16v scores_t(const Stage& st, const half8 q[8], const half8& ones9,
-                                             const half8& q9, int hb, int l32) {
-  float16v s = offset_start(ones9, q9);
+__device__ __forceinline__ float16v scores_t(const Stage& st, const half8 q[8],
+                                             const float16v& s_init, int hb, int l32) {
+  float16v s = s_init;
   const _Float16* krow = st.k + l32 * kKRow + 8 * hb;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -328,7 +323,7 @@ struct ConsState {
   float16v o[4];      // O^T (128 dims x this wave's 32 rows), scaled by 2^6
   float16v s_cur;     // S^T of the current chunk (issued in the previous iteration)
   half8 q[8];          // this lane's Q operands (FP16), for every chunk
-  half8 ones9, q9;     // operands of the chain's first MFMA (adds -1152 sum(Q))
+  float16v s_init;    // every S^T chain's start: -1152 sum(Q) of this lane's row
   half8 pb[2];        // P'^T of the previous chunk
   half8 vfrag[8];     // V^T operands of the previous chunk
   float m_run;        // running maximum (log2 domain) of this lane's row
@@ -386,8 +381,8 @@ __device__ __forceinline__ void chain_softmax(ConsState& cs, const Stage& st, co
   lpc = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (j == 0) s_next = offset_start(cs.ones9, cs.q9);
-    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], cs.q[j], s_next, 0, 0, 0);
+    s_next = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfrag[j], cs.q[j], j == 0 ? cs.s_init : s_next,
+                                                    0, 0, 0);
     if (j + 2 < 8) kfrag[j + 2] = *reinterpret_cast<const half8*>(krow + 16 * (j + 2));
     const int r = 2 * j;
     prob_pair(cs, f, j, __builtin_fmaf(cs.s_cur[r], f.k4[r >> 2][r & 3], -cs.m_run),
@@ -541,7 +536,7 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
     for (int e = 0; e < 8; ++e) cs.pb[ks][e] = (_Float16)0.f;
   {
     // -1152 times the sum of this lane's row of FP16 Q (both lane halves'
-    // dims), as hi + lo in the first MFMA's operands
+    // dims): the accumulator input of every chain's first MFMA
     const half2 one = {(_Float16)1.f, (_Float16)1.f};
     float qs = 0.f;
 #pragma unroll
@@ -550,14 +545,10 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
       for (int e = 0; e < 4; ++e)
         qs = __builtin_amdgcn_fdot2(half2{cs.q[s][2 * e], cs.q[s][2 * e + 1]}, one, qs, false);
     const float init = -1152.f * (qs + __shfl_xor(qs, 32));
-    const _Float16 hi = (_Float16)init;
-    const _Float16 lo = (_Float16)(init - (float)hi);
-    const _Float16 zero = (_Float16)0.f, one1 = (_Float16)(hb == 0 ? 1.f : 0.f);
-    cs.ones9 = half8{one1, one1, zero, zero, zero, zero, zero, zero};
-    cs.q9 = hb == 0 ? half8{hi, lo, zero, zero, zero, zero, zero, zero}
-                    : half8{zero, zero, zero, zero, zero, zero, zero, zero};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cs.s_init[r] = init;
   }
-  cs.s_cur = scores_t(stage(sm, 0), cs.q, cs.ones9, cs.q9, hb, l32);
+  cs.s_cur = scores_t(stage(sm, 0), cs.q, cs.s_init, hb, l32);
   {
     // the running maximum starts at chunk 0's maximum over this row's chosen
     // cells, so that the first chunk needs no rescale (the sinks lead the union)
