@@ -137,6 +137,45 @@ def _short(name: str) -> str:
     return name.split("(")[0].split("<")[0].split("::")[-1]
 
 
+def _sq_summary(d: str, kernels):
+    """Mean per dispatch of every SQ counter that the sq1..sq3 passes of
+    profile.sh took for each kernel, plus ratios of them: matrix-core busy
+    cycles per SIMD-cycle of busy CUs (4 SIMDs per CU), the share of those in
+    which VALU work ran beside the matrix core, and instruction counts per
+    wave."""
+    out = {}
+    for sub in ("sq1", "sq2", "sq3"):
+        path = os.path.join(d, sub, "pmc_counter_collection.csv")
+        if not os.path.exists(path):
+            return None
+        for r in _csv_rows(path):
+            k = _short(r["Kernel_Name"])
+            if k not in kernels:
+                continue
+            acc = out.setdefault(k, {}).setdefault(r["Counter_Name"], {})
+            acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    res = {}
+    for k, counters in out.items():
+        c = {name: float(np.mean(list(v.values()))) for name, v in counters.items()}
+        waves = c.get("SQ_WAVES", 0.0)
+        derived = {}
+        if c.get("SQ_BUSY_CU_CYCLES"):
+            derived["matrix-core busy / (4 x CU busy cycles)"] = \
+                c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4.0 * c["SQ_BUSY_CU_CYCLES"])
+        if c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            derived["VALU beside matrix core / matrix-core busy"] = \
+                c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        if waves:
+            for name in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32"):
+                if name in c:
+                    derived[name + " per wave"] = c[name] / waves
+        if c.get("SQ_ACTIVE_INST_LDS"):
+            derived["LDS bank-conflict cycles / LDS active cycles"] = \
+                c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_ACTIVE_INST_LDS"]
+        res[k] = {"counters": c, "derived": derived}
+    return res
+
+
 def summarize(d: str, workload: str, op: str = "path"):
     """Summaries of a profile.sh run: the kernel-trace statistics as text, and the
     HBM bytes per launch of the op's kernels from FETCH_SIZE / WRITE_SIZE, each
@@ -189,6 +228,19 @@ def summarize(d: str, workload: str, op: str = "path"):
         lines.append("%-28s FETCH %.0f KiB -> %.1f MB, WRITE %.0f KiB -> %.1f MB, total %.1f MB" % (
             k, ent["FETCH_SIZE_KiB_per_dispatch"], ent["fetch_bytes"] / 1e6,
             ent["WRITE_SIZE_KiB_per_dispatch"], ent["write_bytes"] / 1e6, ent["hbm_bytes"] / 1e6))
+    sq = _sq_summary(d, kernels)
+    if sq:
+        rec["sq"] = sq
+        lines += ["", "SQ counters per dispatch (three --pmc runs of at most 8 SQ counters each):"]
+        lines += ["command: " + c for c in commands[3:6]]
+        for k, ent in sq.items():
+            lines.append("%s:" % k)
+            for name in sorted(ent["counters"]):
+                lines.append("  %-28s %16.6g" % (name, ent["counters"][name]))
+            for name, v in ent["derived"].items():
+                lines.append("  %-44s %10.4g" % (name, v))
+        with open(os.path.join(ROOT, "profiles", counters_name), "w") as f:
+            json.dump(rec, f, indent=1)
     lines.append("kernel sources: sha256 prefix %s (the benchmark uses these bytes only while it "
                  "matches)" % rec["source_hash"])
     extra = ("" if op == "path" else " --op " + op) + \
