@@ -21,7 +21,9 @@
 //     through the page table and gathers the INT8 K/V rows with 16-byte loads,
 //     every read consumed kLead iterations after it was issued, converts the
 //     rows to FP16 and stores them into LDS (K tiles in two stages, V tiles and
-//     per-cell factors in four); the consumers only read LDS;
+//     per-cell factors in four); a chunk's V tile and factors are stored one
+//     iteration after its K tile, at the start of an iteration, so that only the
+//     K stores are waited for at the barrier; the consumers only read LDS;
 //   * row n of the 96 = 8*hq + i (query head h*12+hq, position 8g+i), so the
 //     chooser bit of row n is n & 7; consumer wave w owns row block w (32 rows)
 //     and every cell of each chunk, with its own softmax state;
@@ -639,13 +641,18 @@ __device__ __forceinline__ uint2 keep_words(uint32_t x, int b) {
   return uint2{__builtin_amdgcn_perm(lo, hi, 0x08080a0au), __builtin_amdgcn_perm(lo, hi, 0x09090b0bu)};
 }
 
-__device__ __forceinline__ void convert(const PrefillArgs& a, const Stage& st, int ptid, bool kwave,
-                                        const Raw& r, uint32_t& flags) {
+// K tile of a chunk (read by the consumers' S^T chain in the next iteration)
+__device__ __forceinline__ void convert_k(const Stage& st, int ptid, const Raw& r) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    store_k_task(st, ptid + 64 * k, r.k[k]);
-    store_v_task(st, ptid + 64 * k, r.v[k]);
-  }
+  for (int k = 0; k < 4; ++k) store_k_task(st, ptid + 64 * k, r.k[k]);
+}
+
+// V tile, k and v factors and keep masks of a chunk (read by the consumers two
+// iterations later than its K tile)
+__device__ __forceinline__ void convert_v(const PrefillArgs& a, const Stage& st, int ptid, bool kwave,
+                                          const Raw& r, uint32_t& flags) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) store_v_task(st, ptid + 64 * k, r.v[k]);
   // the lower lane half stores the k factors, the upper the v factors
   const int lane = ptid & (kChunk - 1);
   const float sc = r.m ? r.sc : 0.f;
@@ -680,20 +687,25 @@ struct ProdState {
 };
 
 // Iteration c (phase P = c & 3), while the consumers work on chunks c-1..c+1.
+// It opens with the V tile and factors of chunk c+1, so that those stores drain
+// while the rest of the iteration runs, and closes with the K tile of chunk c+2,
+// the only stores the consumers need right after this iteration's barrier.
 // Reads are issued union, page, gather (oldest consumer first), and each one
-// issued here is consumed kLead iterations later.
+// issued here is consumed kLead iterations later; the gather of chunk c+5 reuses
+// the register set that chunk c+1's V conversion has just emptied.
 template <int P>
 __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, ProdState& ps, int c,
                                              int h, int U, int64_t ubase, int ptid, bool translator,
                                              uint32_t& flags) {
   const int lane = ptid & (kChunk - 1);
+  convert_v(a, stage(sm, P + 1), ptid, translator, ps.raw[(P + 1) & 3], flags);
   ps.un[(P + kAheadUnion) & 3] = read_union_entry(a, ubase, U, c + kAheadUnion, lane);
   ps.pg[(P + kAheadPage) & 3] = read_page_entry(a, ps.un[(P + kAheadPage) & 3]);
   const int cf = c + kAheadFinish;
   finish_translation(a, ps.pg[(P + kAheadFinish) & 3], U, cf, h,
                      sm.ring[translator ? (cf & (kRing - 1)) : kRing], lane, flags);
   gather(a, sm.ring[(c + kAheadGather) & (kRing - 1)], ptid, ps.raw[(P + kAheadGather) & 3]);
-  convert(a, stage(sm, P + 2), ptid, translator, ps.raw[(P + 2) & 3], flags);
+  convert_k(stage(sm, P + 2), ptid, ps.raw[(P + 2) & 3]);
   lds_barrier();
 }
 
@@ -725,14 +737,17 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
       finish_translation(a, p[i], U, i, h, sm.ring[translator ? i : kRing], lane, flags);
   }
   lds_barrier();
+  static_assert(kAheadGather == 5, "the prologue stages chunk 0 before gathering chunk 4");
 #pragma unroll
   for (int x = 0; x < kAheadGather; ++x) {
-    if (x >= 4) convert(a, stage(sm, x - 4), ptid, translator, ps.raw[x & 3], flags);   // frees the set
+    if (x == 4) {   // chunk 0 in full, which frees its register set
+      convert_k(stage(sm, 0), ptid, ps.raw[0]);
+      convert_v(a, stage(sm, 0), ptid, translator, ps.raw[0], flags);
+    }
     gather(a, sm.ring[x], ptid, ps.raw[x & 3]);
   }
-#pragma unroll
-  for (int x = (kAheadGather > 4 ? kAheadGather - 4 : 0); x < 2; ++x)
-    convert(a, stage(sm, x), ptid, translator, ps.raw[x & 3], flags);
+  // chunk 1's K tile (its V tile and factors open iteration 0)
+  convert_k(stage(sm, 1), ptid, ps.raw[1]);
   lds_barrier();
   lds_barrier();   // the consumers have read chunk 0's K tile
 
