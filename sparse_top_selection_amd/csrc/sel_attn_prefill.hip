@@ -18,8 +18,9 @@
 //     walks consecutive groups of one KV head;
 //   * waves 0..2 consume, wave 3 produces (at raised priority: every wave waits
 //     for its stage at the barrier). The producer translates union cells
-//     through the page table and gathers the INT8 K/V rows with 16-byte loads,
-//     every read consumed kLead iterations after it was issued, converts the
+//     through the page table (two chunks at a time, every other iteration) and
+//     gathers the INT8 K/V rows with 16-byte loads, every read consumed at
+//     least kLead iterations after it was issued, converts the
 //     rows to FP16 and stores them into LDS (K tiles in two stages, V tiles and
 //     per-cell factors in four); a chunk's V tile and factors are stored one
 //     iteration after its K tile, at the start of an iteration, so that only the
@@ -96,7 +97,7 @@ struct __align__(16) Smem {
   float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
   _Float16 vf[kStages][kChunk];         // FP16(v_scale * 2^9); 0 where unusable
   uint32_t keep[kStages][4 * kChunk];   // keep masks, 16-byte units laid out by keep_unit()
-  Ring ring[kRing + 1];   // the last slot takes the upper producer lanes' copies
+  Ring ring[kRing];
 };
 // two work-groups share a CU (LDS 160 KB): one's prologue and epilogue overlap
 // the other's chunk loop
@@ -220,11 +221,12 @@ __device__ __forceinline__ void store_v_task(const Stage& st, int t, u32x4 raw) 
 }
 
 // ---------------------------------------------------------------------------
-// Page translation of one chunk cell (one lane per cell), in three steps whose
-// global reads are each consumed kLead iterations after they were issued (the
-// same lead as the K/V gathers, so that no wait for an early read also waits
-// for gathers still in flight): read the union entry, then the page-table
-// entry, then form the pool row and publish it in the ring.
+// Page translation of one chunk cell (one lane per cell; the two lane halves
+// take the two chunks of a pair), in three steps whose global reads are each
+// consumed four iterations after they were issued (at least the lead of the
+// K/V gathers, so that no wait for an early read also waits for gathers still
+// in flight): read the union entry, then the page-table entry, then form the
+// pool row and publish it in the ring.
 // Records carry only loaded words (each in a register of its own: packing a
 // field next to another would read the in-flight load at once); whether an
 // entry lies inside the union is recomputed from the chunk index.
@@ -597,13 +599,13 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 
 // ---------------------------------------------------------------------------
 // Producer wave 3 (64 threads, ptid = tid - 192). Iteration c (while the
-// consumers work on chunks c and c+1): read the union entries of chunk
-// c+kAheadUnion, the page-table entries of chunk c+kAheadPage, publish the
-// pool rows of chunk c+kAheadFinish in the ring, gather chunk c+kAheadGather
-// into registers and convert chunk c+2 (gathered kLead iterations earlier) into
-// its LDS stages. Each thread owns tasks ptid + 64k (k = 0..3) of both pools,
-// and the k scale (ptid < 32) or v scale of cell ptid & 31; both lane halves
-// translate cell ptid & 31, the lower half into the ring.
+// consumers work on chunks c and c+1): store chunk c+1's V tile and factors,
+// on even c translate a pair of chunks (union entries of c+14, c+15, page-table
+// entries of c+10, c+11, ring slots of c+6, c+7; lane half hb takes the pair's
+// chunk hb, cell ptid & 31), gather chunk c+kAheadGather into registers and
+// store the K tile of chunk c+2 (gathered kLead iterations earlier). Each
+// thread owns tasks ptid + 64k (k = 0..3) of both pools, and the k scale
+// (ptid < 32) or v scale of cell ptid & 31.
 struct Raw {
   u32x4 k[4];
   u32x4 v[4];
@@ -676,14 +678,21 @@ __device__ __forceinline__ void convert_v(const PrefillArgs& a, const Stage& st,
 // a compile-time constant once a step is instantiated for its phase P = c & 3,
 // so the sets stay in registers and the stage addresses fold into immediates.
 constexpr int kAheadGather = 2 + kLead;        // chunk gathered in iteration c: c + 5
-constexpr int kAheadFinish = 3 + kLead;        // ring slot written: c + 6
-constexpr int kAheadPage = 3 + 2 * kLead;      // page entry read: c + 9
-constexpr int kAheadUnion = 3 + 3 * kLead;     // union entry read: c + 12
+// Translation runs on even iterations c, for a pair of chunks at once (lane
+// half hb takes chunk 2m + hb of pair m): the ring slots of pair c+6, c+7 are
+// written from page records read four iterations earlier, whose union records
+// were read four iterations before that. Chunk x's slot is thus written one or
+// two iterations before x is gathered (x - 5).
+constexpr int kPairFinish = 6;                 // pair whose ring slots are written: c + 6, c + 7
+constexpr int kPairPage = 10;                  // pair whose page entries are read: c + 10, c + 11
+constexpr int kPairUnion = 14;                 // pair whose union entries are read: c + 14, c + 15
+static_assert(kAheadGather < kPairFinish && kPairFinish + 1 < kAheadGather + kRing,
+              "ring slots are written before their gather and kept until it");
 
 struct ProdState {
   Raw raw[4];
-  UnionRec un[4];
-  PageRec pg[4];
+  UnionRec un[2];   // by pair parity
+  PageRec pg[2];
 };
 
 // Iteration c (phase P = c & 3), while the consumers work on chunks c-1..c+1.
@@ -699,11 +708,16 @@ __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, Pro
                                              uint32_t& flags) {
   const int lane = ptid & (kChunk - 1);
   convert_v(a, stage(sm, P + 1), ptid, translator, ps.raw[(P + 1) & 3], flags);
-  ps.un[(P + kAheadUnion) & 3] = read_union_entry(a, ubase, U, c + kAheadUnion, lane);
-  ps.pg[(P + kAheadPage) & 3] = read_page_entry(a, ps.un[(P + kAheadPage) & 3]);
-  const int cf = c + kAheadFinish;
-  finish_translation(a, ps.pg[(P + kAheadFinish) & 3], U, cf, h,
-                     sm.ring[translator ? (cf & (kRing - 1)) : kRing], lane, flags);
+  if constexpr ((P & 1) == 0) {
+    // pairs c/2 + 3, + 5 and + 7 share a parity: each record set is consumed
+    // before it is refilled
+    constexpr int s = (P / 2 + 1) & 1;
+    const int hb = ptid >> 5;
+    const int cf = c + kPairFinish + hb;
+    finish_translation(a, ps.pg[s], U, cf, h, sm.ring[cf & (kRing - 1)], lane, flags);
+    ps.pg[s] = read_page_entry(a, ps.un[s]);
+    ps.un[s] = read_union_entry(a, ubase, U, c + kPairUnion + hb, lane);
+  }
   gather(a, sm.ring[(c + kAheadGather) & (kRing - 1)], ptid, ps.raw[(P + kAheadGather) & 3]);
   convert_k(stage(sm, P + 2), ptid, ps.raw[(P + 2) & 3]);
   lds_barrier();
@@ -712,29 +726,29 @@ __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, Pro
 __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, int U, int nch,
                                         int64_t ubase, int ptid, bool translator,
                                         uint32_t& flags) {
-  static_assert(kLead >= 1 && kLead <= 3 && kStages == 4 && kAheadFinish <= kRing,
-                "register sets and ring slots cover the lead");
+  static_assert(kLead >= 1 && kLead <= 3 && kStages == 4, "register sets cover the lead");
+  static_assert(kPairFinish == 6 && kPairPage == 10 && kPairUnion == 14, "the prologue below");
   const int lane = ptid & (kChunk - 1);
+  const int hb = ptid >> 5;
   ProdState ps;
-  // prologue: what iteration 0 expects. Chunks below kAheadFinish translated
-  // into their ring slots; page records of the next kLead chunks and union
-  // records of the kLead after those read; chunks 0 and 1 staged, chunks 2 ..
-  // kAheadGather-1 gathered. Both lane halves translate the same cells; the
-  // upper half writes its copy to the spare slot.
+  // prologue: what iteration 0 expects. Pairs 0..2 (chunks 0..5) translated
+  // into their ring slots; page records of pairs 3 and 4 and union records of
+  // pairs 5 and 6 read (sets by pair parity); chunk 0 staged, chunk 1's K tile
+  // staged, chunks 1 .. kAheadGather-1 gathered.
   {
-    UnionRec u[kAheadPage];
+    UnionRec u[5];
 #pragma unroll
-    for (int i = 0; i < kAheadPage; ++i) u[i] = read_union_entry(a, ubase, U, i, lane);
+    for (int m = 0; m < 5; ++m) u[m] = read_union_entry(a, ubase, U, 2 * m + hb, lane);
+    ps.un[1] = read_union_entry(a, ubase, U, 2 * 5 + hb, lane);
+    ps.un[0] = read_union_entry(a, ubase, U, 2 * 6 + hb, lane);
+    PageRec p[3];
 #pragma unroll
-    for (int i = kAheadPage; i < kAheadUnion; ++i) ps.un[i & 3] = read_union_entry(a, ubase, U, i, lane);
-    PageRec p[kAheadFinish];
+    for (int m = 0; m < 3; ++m) p[m] = read_page_entry(a, u[m]);
+    ps.pg[1] = read_page_entry(a, u[3]);
+    ps.pg[0] = read_page_entry(a, u[4]);
 #pragma unroll
-    for (int i = 0; i < kAheadFinish; ++i) p[i] = read_page_entry(a, u[i]);
-#pragma unroll
-    for (int i = kAheadFinish; i < kAheadPage; ++i) ps.pg[i & 3] = read_page_entry(a, u[i]);
-#pragma unroll
-    for (int i = 0; i < kAheadFinish; ++i)
-      finish_translation(a, p[i], U, i, h, sm.ring[translator ? i : kRing], lane, flags);
+    for (int m = 0; m < 3; ++m)
+      finish_translation(a, p[m], U, 2 * m + hb, h, sm.ring[2 * m + hb], lane, flags);
   }
   lds_barrier();
   static_assert(kAheadGather == 5, "the prologue stages chunk 0 before gathering chunk 4");
