@@ -12,7 +12,8 @@
 // gfx950 design: one work-group per query position, 4 waves.
 // Phase 1 (the whole work-group) turns the selection row into a list of pool
 // rows, then the work-group synchronises once:
-// - repeats are dropped through an LDS hash that keeps each cell's first entry;
+// - repeats are dropped through an LDS hash that keeps each cell's first entry
+//   (a strictly ascending row, which has none, skips the hash);
 // - cells out of range and non-resident pages are dropped;
 // - the kept entries are compacted in row order.
 // Phase 2: wave w handles KV heads w, w+4, ... (12 query rows each) over the
@@ -307,39 +308,43 @@ __device__ __forceinline__ int build_list(const PositionsArgs& a, Smem& sm, int 
   }
   const int32_t* srow = a.sel + (int64_t)j * a.sel_cap;
 
-  for (int s = tid; s < kHashSlots; s += kThreads) {
-    hash_key[s] = -1;
-    hash_first[s] = 0x7fffffff;
-  }
   int32_t cell[kPer];
+  bool asc = true;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int e = tid + kThreads * k;
     cell[k] = e < L ? srow[e] : -1;
+    const int32_t next = e + 1 < L ? srow[e + 1] : 0;
+    asc = asc && (e + 1 >= L || cell[k] < next);
+    if (e < L && (cell[k] < 0 || cell[k] >= a.n_ctx)) flags |= SEL_ATTN_STATUS_CELL_RANGE;
   }
-  __syncthreads();
+  // a strictly ascending row has no repeats; any other row goes through the hash
+  const bool sorted = __syncthreads_and(asc);
+  if (!sorted) {
+    for (int s = tid; s < kHashSlots; s += kThreads) {
+      hash_key[s] = -1;
+      hash_first[s] = 0x7fffffff;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int e = tid + kThreads * k;
-    if (e >= L) continue;
-    const int32_t c = cell[k];
-    if (c < 0 || c >= a.n_ctx) {
-      flags |= SEL_ATTN_STATUS_CELL_RANGE;
-      continue;
-    }
-    // at most kPer * kThreads < kHashSlots distinct cells: an empty slot or
-    // the cell itself is always found
-    uint32_t s = hash_slot(c);
-    while (true) {
-      const int32_t prev = atomicCAS(&hash_key[s], -1, c);
-      if (prev == -1 || prev == c) {
-        atomicMin(&hash_first[s], e);
-        break;
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + kThreads * k;
+      const int32_t c = cell[k];
+      if (e >= L || c < 0 || c >= a.n_ctx) continue;
+      // at most kPer * kThreads < kHashSlots distinct cells: an empty slot or
+      // the cell itself is always found
+      uint32_t s = hash_slot(c);
+      while (true) {
+        const int32_t prev = atomicCAS(&hash_key[s], -1, c);
+        if (prev == -1 || prev == c) {
+          atomicMin(&hash_first[s], e);
+          break;
+        }
+        s = (s + 1) & (kHashSlots - 1);
       }
-      s = (s + 1) & (kHashSlots - 1);
     }
+    __syncthreads();
   }
-  __syncthreads();
   // each cell's first entry looks up its page; all lookups are issued before
   // the first is used (one memory round trip, not one per round)
   int32_t page[kPer];
@@ -349,9 +354,13 @@ __device__ __forceinline__ int build_list(const PositionsArgs& a, Smem& sm, int 
     const int32_t c = cell[k];
     page[k] = -1;
     if (e < L && c >= 0 && c < a.n_ctx) {
-      uint32_t s = hash_slot(c);
-      while (hash_key[s] != c) s = (s + 1) & (kHashSlots - 1);
-      if (hash_first[s] == e) page[k] = a.page_table[c >> 6];
+      bool first = true;
+      if (!sorted) {
+        uint32_t s = hash_slot(c);
+        while (hash_key[s] != c) s = (s + 1) & (kHashSlots - 1);
+        first = hash_first[s] == e;
+      }
+      if (first) page[k] = a.page_table[c >> 6];
       else cell[k] = -1;                 // a repeat
     }
   }
@@ -415,11 +424,84 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(Position
 // ---------------------------------------------------------------------------
 // Decode: a few positions (one, or a speculative verify window), each split
 // over its cells so that the GPU has enough work-groups. Work-group (s, j)
-// builds position j's list (every split of a position builds the same list)
-// and attends to entries [64s, 64s + 64) of it for every KV head. It writes
+// takes the kept cells among entries [64s, 64s + 64) of position j's row and
+// attends to them for every KV head. It writes
 // the split's unnormalised state; a second kernel merges the splits of each
 // (position, head) in the usual way: weights exp2(m_s - max m), sums of those
 // times O_s and l_s, then O / l.
+
+// Decode split s of position j: the kept cells among the row's entries
+// [64s, 64s + 64), in entry order, in sm.rows. A cell counts at its first entry
+// in the row: a strictly ascending row has no repeats; any other row goes
+// through the LDS hash, which keeps each cell's first entry. Cells out of range
+// (checked over the whole row, as every split reports them) and non-resident
+// pages are dropped. Returns the count.
+__device__ __forceinline__ int build_split_list(const PositionsArgs& a, Smem& sm, int j, int first,
+                                                int tid, int lane, int wave, uint32_t& flags) {
+  int32_t* hash_key = sm.u.hash.key;
+  int32_t* hash_first = sm.u.hash.first;
+  int L = a.sel_len[j];
+  if (L < 0 || L > a.sel_cap) {
+    flags |= SEL_ATTN_STATUS_SEL_LEN;
+    L = L < 0 ? 0 : a.sel_cap;
+  }
+  const int32_t* srow = a.sel + (int64_t)j * a.sel_cap;
+  int32_t cell[kPer];
+  bool asc = true;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = tid + kThreads * k;
+    cell[k] = e < L ? srow[e] : -1;
+    const int32_t next = e + 1 < L ? srow[e + 1] : 0;
+    asc = asc && (e + 1 >= L || cell[k] < next);
+    if (e < L && (cell[k] < 0 || cell[k] >= a.n_ctx)) flags |= SEL_ATTN_STATUS_CELL_RANGE;
+  }
+  const bool sorted = __syncthreads_and(asc);
+  if (!sorted) {
+    for (int s = tid; s < kHashSlots; s += kThreads) {
+      hash_key[s] = -1;
+      hash_first[s] = 0x7fffffff;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = tid + kThreads * k;
+      const int32_t c = cell[k];
+      if (e >= L || c < 0 || c >= a.n_ctx) continue;
+      // at most kPer * kThreads < kHashSlots distinct cells: an empty slot or
+      // the cell itself is always found
+      uint32_t s = hash_slot(c);
+      while (true) {
+        const int32_t prev = atomicCAS(&hash_key[s], -1, c);
+        if (prev == -1 || prev == c) {
+          atomicMin(&hash_first[s], e);
+          break;
+        }
+        s = (s + 1) & (kHashSlots - 1);
+      }
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    const int e = first + lane;
+    const int32_t c = e < L ? srow[e] : -1;
+    bool counts = e < L && c >= 0 && c < a.n_ctx;
+    if (counts && !sorted) {
+      uint32_t s = hash_slot(c);
+      while (hash_key[s] != c) s = (s + 1) & (kHashSlots - 1);
+      counts = hash_first[s] == e;
+    }
+    const int32_t page = counts ? a.page_table[c >> 6] : -1;
+    if (counts && (page >= a.n_pages || page < -1)) flags |= SEL_ATTN_STATUS_PAGE_RANGE;
+    const bool keep = counts && page >= 0 && page < a.n_pages;
+    const uint64_t m = __ballot(keep);
+    if (keep)
+      sm.rows[lanes_below(m)] = ((uint32_t)page * (uint32_t)a.n_kv) * 64u + (uint32_t)(c & 63);
+    if (lane == 0) sm.wave_count[0][0] = __popcll(m);
+  }
+  __syncthreads();   // the list is complete; the hash area becomes the waves' tiles
+  return sm.wave_count[0][0];
+}
 
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(PositionsArgs a,
                                                                   DecodePartial* part) {
@@ -430,16 +512,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(PositionsArgs
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t flags = 0;
-  const int n = build_list(a, sm, j, tid, lane, wave, flags);
   const int first = kDecodeSplit * s;
-  const int n_s = max(0, min(kDecodeSplit, n - first));
+  const int n_s = build_split_list(a, sm, j, first, tid, lane, wave, flags);
 
   const int g = lane >> 4, i = lane & 15;
   for (int h = wave; h < a.n_kv; h += kWaves) {
     ChunkState st;
     float l_row, lp_row;
-    attend_range(a, sm.rows + min(first, n), sm.u.tile[wave], j, h, n_s, lane, flags, st, l_row,
-                 lp_row);
+    attend_range(a, sm.rows, sm.u.tile[wave], j, h, n_s, lane, flags, st, l_row, lp_row);
     DecodePartial& p = part[((int64_t)j * a.n_kv + h) * a.n_splits + s];
     if (i < kQPerKv) {
       const float corr = 1152.f * lp_row;

@@ -160,8 +160,10 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
   __syncthreads();   // row_end
 
   int written = 0;  // union cells emitted so far (same value in every thread)
-  int round = 0;
-  for (int w0 = 0; w0 < a.n_ctx; w0 += kWindowCells, ++round) {
+  // windows counted, not stepped, so that no cell index passes INT32_MAX
+  const int n_windows = (int)(((int64_t)a.n_ctx + kWindowCells - 1) / kWindowCells);
+  for (int round = 0; round < n_windows; ++round) {
+    const int w0 = round * kWindowCells;
     const int win = min(kWindowCells, a.n_ctx - w0);
     // the first batch's loads go out before the bitmap is cleared
     for (int i = tid; i < kWindowWords / 4; i += kThreads)
