@@ -482,9 +482,15 @@ __device__ __forceinline__ int build_split_list(const PositionsArgs& a, Smem& sm
     }
     __syncthreads();
   }
-  if (wave == 0) {
+  // the split's entries first + lane are already in the registers of wave
+  // (first / 64) & 3, at index first / 256
+  const int owner = (first >> 6) & (kWaves - 1);
+  if (wave == owner) {
     const int e = first + lane;
-    const int32_t c = e < L ? srow[e] : -1;
+    const int ks = first >> 8;
+    int32_t c = -1;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) c = k == ks ? cell[k] : c;
     bool counts = e < L && c >= 0 && c < a.n_ctx;
     if (counts && !sorted) {
       uint32_t s = hash_slot(c);
@@ -536,9 +542,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(PositionsArgs
 }
 
 // One work-group per (query row, KV head, position), one thread per dim.
-// Thread s of the first wave reads split s's m and l (at most 40 splits), the
-// wave reduces them, and the weights go through LDS; then every thread sums
-// its dim over the splits with the loads unrolled.
+// Every thread first issues the loads of its dim in all splits (at most 40);
+// meanwhile thread s of the first wave reads split s's m and l, the wave
+// reduces them, and the weights go through LDS; then every thread sums its dim
+// over the splits. One memory round trip in all.
+constexpr int kMaxSplits = (SEL_ATTN_POSITIONS_MAX_CAP + kDecodeSplit - 1) / kDecodeSplit;
+static_assert(kMaxSplits <= 64, "one wave reduces the splits' maxima");
+
 __global__ __launch_bounds__(kD) void decode_merge_kernel(PositionsArgs a, const DecodePartial* part) {
   __shared__ float wsh[64];
   __shared__ float lsh;
@@ -547,6 +557,9 @@ __global__ __launch_bounds__(kD) void decode_merge_kernel(PositionsArgs a, const
   const int j = blockIdx.z;
   const int d = threadIdx.x;
   const DecodePartial* p = part + ((int64_t)j * a.n_kv + h) * a.n_splits;
+  float od[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) od[s] = s < a.n_splits ? p[s].o[r][d] : 0.f;
   if (d < 64) {
     const bool ok = d < a.n_splits;
     const float ms = ok ? p[d].m[r] : kNoMax;
@@ -563,8 +576,8 @@ __global__ __launch_bounds__(kD) void decode_merge_kernel(PositionsArgs a, const
   }
   __syncthreads();
   float acc = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < a.n_splits; ++s) acc += wsh[s] * p[s].o[r][d];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) acc += s < a.n_splits ? wsh[s] * od[s] : 0.f;
   const float l = lsh;
   const int n_qh = a.n_kv * kQPerKv;
   a.out[((int64_t)j * n_qh + h * kQPerKv + r) * kD + d] = l > 0.f ? acc * ((1.f / kVFold) / l) : 0.f;
