@@ -699,15 +699,16 @@ struct ProdState {
 // It opens with the V tile and factors of chunk c+1, so that those stores drain
 // while the rest of the iteration runs, and closes with the K tile of chunk c+2,
 // the only stores the consumers need right after this iteration's barrier.
-// Reads are issued union, page, gather (oldest consumer first), and each one
-// issued here is consumed kLead iterations later; the gather of chunk c+5 reuses
-// the register set that chunk c+1's V conversion has just emptied.
+// Reads are issued page, union, gather; translation reads are consumed four
+// iterations later, gathers kLead; the gather of chunk c+5 reuses the register
+// set that chunk c+1's V conversion has just emptied. `lower` (ptid < 32): this
+// lane stores k factors, else v factors.
 template <int P>
 __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, ProdState& ps, int c,
-                                             int h, int U, int64_t ubase, int ptid, bool translator,
+                                             int h, int U, int64_t ubase, int ptid, bool lower,
                                              uint32_t& flags) {
   const int lane = ptid & (kChunk - 1);
-  convert_v(a, stage(sm, P + 1), ptid, translator, ps.raw[(P + 1) & 3], flags);
+  convert_v(a, stage(sm, P + 1), ptid, lower, ps.raw[(P + 1) & 3], flags);
   if constexpr ((P & 1) == 0) {
     // pairs c/2 + 3, + 5 and + 7 share a parity: each record set is consumed
     // before it is refilled
@@ -724,7 +725,7 @@ __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, Pro
 }
 
 __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, int U, int nch,
-                                        int64_t ubase, int ptid, bool translator,
+                                        int64_t ubase, int ptid, bool lower,
                                         uint32_t& flags) {
   static_assert(kLead >= 1 && kLead <= 3 && kStages == 4, "register sets cover the lead");
   static_assert(kPairFinish == 6 && kPairPage == 10 && kPairUnion == 14, "the prologue below");
@@ -756,7 +757,7 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
   for (int x = 0; x < kAheadGather; ++x) {
     if (x == 4) {   // chunk 0 in full, which frees its register set
       convert_k(stage(sm, 0), ptid, ps.raw[0]);
-      convert_v(a, stage(sm, 0), ptid, translator, ps.raw[0], flags);
+      convert_v(a, stage(sm, 0), ptid, lower, ps.raw[0], flags);
     }
     gather(a, sm.ring[x], ptid, ps.raw[x & 3]);
   }
@@ -767,15 +768,15 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
 
   int c = 0;
   for (; c + 4 <= nch; c += 4) {
-    produce_step<0>(a, sm, ps, c, h, U, ubase, ptid, translator, flags);
-    produce_step<1>(a, sm, ps, c + 1, h, U, ubase, ptid, translator, flags);
-    produce_step<2>(a, sm, ps, c + 2, h, U, ubase, ptid, translator, flags);
-    produce_step<3>(a, sm, ps, c + 3, h, U, ubase, ptid, translator, flags);
+    produce_step<0>(a, sm, ps, c, h, U, ubase, ptid, lower, flags);
+    produce_step<1>(a, sm, ps, c + 1, h, U, ubase, ptid, lower, flags);
+    produce_step<2>(a, sm, ps, c + 2, h, U, ubase, ptid, lower, flags);
+    produce_step<3>(a, sm, ps, c + 3, h, U, ubase, ptid, lower, flags);
   }
   const int rem = nch - c;   // 0..3 more iterations, phases 0, 1, 2
-  if (rem > 0) produce_step<0>(a, sm, ps, c, h, U, ubase, ptid, translator, flags);
-  if (rem > 1) produce_step<1>(a, sm, ps, c + 1, h, U, ubase, ptid, translator, flags);
-  if (rem > 2) produce_step<2>(a, sm, ps, c + 2, h, U, ubase, ptid, translator, flags);
+  if (rem > 0) produce_step<0>(a, sm, ps, c, h, U, ubase, ptid, lower, flags);
+  if (rem > 1) produce_step<1>(a, sm, ps, c + 1, h, U, ubase, ptid, lower, flags);
+  if (rem > 2) produce_step<2>(a, sm, ps, c + 2, h, U, ubase, ptid, lower, flags);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void sel_attn_prefill_kernel(PrefillArgs a) {
