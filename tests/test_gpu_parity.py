@@ -159,6 +159,18 @@ def test_attention_random_selections_all_rows(seed, n_ctx, n_q, n_kv, dup, nonre
     assert np.all(out[empty] == 0)
 
 
+@pytest.mark.parametrize("seed,n_ctx,n_q,n_kv,cap", [(25, 3000, 27, 2, 37), (26, 5001, 19, 1, 3001),
+                                                     (27, 130, 11, 3, 5)])
+def test_attention_other_row_strides(seed, n_ctx, n_q, n_kv, cap):
+    """Selection rows (and so union rows, 8 * sel_cap) of other strides; contexts
+    that end inside a page; ragged last groups; repeats and non-resident pages."""
+    print("case", seed, n_ctx, n_q, n_kv, cap, flush=True)
+    d = synth.small_random(seed, n_ctx=n_ctx, n_q=n_q, n_kv=n_kv, sel_cap=cap, dup_frac=0.2,
+                           nonresident_frac=0.2, pool_extra=1)
+    assert d["sel"].shape == (n_q, cap)
+    _check_problem(d, what="row stride %d" % cap)
+
+
 def test_attention_empty_groups_and_chunk_remainders():
     """Groups whose union is empty (every position selected nothing: the chunk
     loop runs zero times) next to groups whose unions end in every position of
