@@ -20,11 +20,11 @@
 //     for its stage at the barrier). The producer translates union cells
 //     through the page table (two chunks at a time, every other iteration) and
 //     gathers the INT8 K/V rows with 16-byte loads, every read consumed at
-//     least kLead iterations after it was issued, converts the
-//     rows to FP16 and stores them into LDS (K tiles in two stages, V tiles and
-//     per-cell factors in four); a chunk's V tile and factors are stored one
-//     iteration after its K tile, at the start of an iteration, so that only the
-//     K stores are waited for at the barrier; the consumers only read LDS;
+//     least kLead iterations after it was issued, converts the rows to FP16
+//     and stores them into LDS (K tiles in two stages, V tiles and per-cell
+//     factors in four); a chunk's V tile and factors are stored one iteration
+//     after its K tile, at the start of an iteration, so that only the K
+//     stores are waited for at the barrier; the consumers only read LDS;
 //   * row n of the 96 = 8*hq + i (query head h*12+hq, position 8g+i), so the
 //     chooser bit of row n is n & 7; consumer wave w owns row block w (32 rows)
 //     and every cell of each chunk, with its own softmax state;
@@ -40,9 +40,10 @@
 //     matrix pipe and the VALU work at the same time;
 //   * K and V integers (plus the +1152 offset of the byte-to-FP16 trick) are
 //     exact in FP16; the K offset is removed by starting each S^T chain from
-//     -1152 sum(Q) of its row (FP32, kept in registers), k_scale * softmax_scale * log2(e) multiplies
-//     the score in FP32, and the FP16 probabilities are multiplied by the FP16
-//     v factor v_scale * 2^6 (2^-6 returns in the epilogue). Each lane tracks
+//     -1152 sum(Q) of its row (FP32, kept in registers); k_scale *
+//     softmax_scale * log2(e) multiplies the score in FP32, and the FP16
+//     probabilities are multiplied by the FP16 v factor v_scale * 2^6 (2^-6
+//     returns in the epilogue). Each lane tracks
 //     the sum of the P' values it feeds the MFMA; 1152 times that sum (the V
 //     offset) is removed once at the end;
 //   * keep masks: the producers expand the chooser bytes into 16-bit all-ones
