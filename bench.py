@@ -90,6 +90,18 @@ OP_SOURCES = {"path": ("union_build.hip", "sel_attn_prefill.hip"),
               "decode": ("prefill_positions.hip",)}
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def source_hash(op: str = "path") -> str:
     """Hash of the op's kernel sources and the shared argument header: counters
     taken on other bytes are not used."""
@@ -445,7 +457,20 @@ def main():
             "sample": "query positions 0..%d of the same chunk (%d of %d), FP64 per-position "
                       "gather, %.1f s" % (n_rows - 1, n_rows, w.n_q, cpu_s),
             "positions_per_s": n_rows / cpu_s,
+            "cpu_model": _cpu_model(),
         }
+        # the same oracle on one thread, over a sixteenth of the sample
+        n1 = max(1, min(n_rows, n_rows // 16))
+        c0 = time.perf_counter()
+        oracle.attention_of(inp, rows=rows[:n1], n_threads=1)
+        one_s = time.perf_counter() - c0
+        one_cells = 0
+        for j in rows[:n1]:
+            row = np.unique(sel[j, :sel_len[j]])
+            one_cells += int(np.count_nonzero(pt[row // 64] >= 0))
+        result["cpu_baseline"]["one_core"] = {
+            "value": one_cells * w.n_qh / one_s, "positions_per_s": n1 / one_s,
+            "sample": "query positions 0..%d, %.1f s" % (n1 - 1, one_s)}
         result["parity_on_cpu_sample"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
                                           "out_rms": float(np.sqrt(np.mean(ref ** 2)))}
     print(json.dumps(result), flush=True)
@@ -544,7 +569,7 @@ def bench_decode(args):
         cpu_s = (time.perf_counter() - c0) / reps
         err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
         result["cpu_baseline"] = {"value": cpu_s * 1e6, "unit": "us", "cores": cores,
-                                  "kind": "oracle",
+                                  "kind": "oracle", "cpu_model": _cpu_model(),
                                   "sample": "the same %d position(s), FP64, %d repeats" % (nd, reps)}
         result["parity_on_cpu_sample"] = {"max_abs": float(err.max()), "mean_abs": float(err.mean())}
     print(json.dumps(result), flush=True)
@@ -648,6 +673,7 @@ def bench_select(args):
         same = bool(np.array_equal(lens[:n_rows], ref_len) and np.array_equal(got[valid], ref[valid]))
         result["cpu_baseline"] = {
             "value": n_rows / cpu_s, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": "positions %d..%d (%d rows), numpy per-row sort, %.1f s" % (
                 first, first + n_rows - 1, n_rows, cpu_s)}
         result["parity_on_cpu_sample"] = {"rows_bit_exact": same}
