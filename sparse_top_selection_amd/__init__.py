@@ -192,6 +192,20 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, device):
         raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
 
 
+def _need_shape(t, name: str, dtype, shape, device):
+    """A caller-supplied output: dtype, exact shape, contiguous, on the device."""
+    _need(t, name, dtype, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _status_for(status, device) -> torch.Tensor:
+    if status is None:
+        return new_status(device)
+    _need_shape(status, "status", torch.int32, (1,), device)
+    return status
+
+
 def new_status(device) -> torch.Tensor:
     return torch.zeros(1, dtype=torch.int32, device=device)
 
@@ -222,9 +236,9 @@ def select_blocks(block_scores: torch.Tensor, first_pos: int, n_ctx: int,
     else:
         sel, sel_len = out
         _need(sel, "sel", torch.int32, 2, dev)
-        _need(sel_len, "sel_len", torch.int32, 1, dev)
-        if sel.shape[0] != n_q or sel_len.shape[0] != n_q:
-            raise ValueError("sel and sel_len must have n_q rows")
+        _need_shape(sel_len, "sel_len", torch.int32, (n_q,), dev)
+        if sel.shape[0] != n_q:
+            raise ValueError("sel must have n_q rows")
         sel_cap = sel.shape[1]
     dims = make_dims(n_ctx, n_q, 1, 1, sel_cap=sel_cap)
     sel_attn_select_blocks(dims, first_pos, block_scores, sel, sel_len, stream)
@@ -247,8 +261,10 @@ def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, status=Non
         length = torch.empty(g, dtype=torch.int32, device=dev)
     else:
         cells, mask, length = out
-    if status is None:
-        status = new_status(dev)
+        _need_shape(cells, "union_cells", torch.int32, (g, 8 * cap), dev)
+        _need_shape(mask, "union_mask", torch.uint8, (g, 8 * cap), dev)
+        _need_shape(length, "union_len", torch.int32, (g,), dev)
+    status = _status_for(status, dev)
     dims = make_dims(n_ctx, n_q, 1, 1, sel_cap=cap)
     sel_attn_build_union(dims, sel, sel_len, cells, mask, length, status, stream)
     return cells, mask, length, status
@@ -283,8 +299,9 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
     cap = union_cells.shape[1] // 8
     if out is None:
         out = torch.empty_like(q)
-    if status is None:
-        status = new_status(dev)
+    else:
+        _need_shape(out, "out", torch.float32, q.shape, dev)
+    status = _status_for(status, dev)
     dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=cap, head_dim=hd, page_size=ps)
     sel_attn_prefill(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
                      union_mask, union_len, softmax_scale, out, status, stream)
@@ -321,8 +338,9 @@ def prefill_positions(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_
     dims = _positions_dims(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, n_ctx)
     if out is None:
         out = torch.empty_like(q)
-    if status is None:
-        status = new_status(q.device)
+    else:
+        _need_shape(out, "out", torch.float32, q.shape, q.device)
+    status = _status_for(status, q.device)
     sel_attn_prefill_positions(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
                                softmax_scale, out, status, stream)
     return out, status
@@ -337,10 +355,13 @@ def decode(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, softma
     need = sel_attn_decode_workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1, q.device)
     if out is None:
         out = torch.empty_like(q)
-    if status is None:
-        status = new_status(q.device)
+    else:
+        _need_shape(out, "out", torch.float32, q.shape, q.device)
+    status = _status_for(status, q.device)
     sel_attn_decode(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
                     softmax_scale, out, workspace, workspace.numel() * workspace.element_size(),
                     status, stream)

@@ -177,3 +177,74 @@ def test_builder_loads_without_the_library():
             "assert m.sources(), 'no HIP sources'")
     res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def _small_problem(n_q=10, n_kv=1, n_pages=4, cap=7):
+    import torch
+    return dict(
+        q=torch.zeros((n_q, 12 * n_kv, 128), dtype=torch.float32),
+        k_pool=torch.zeros((n_pages, n_kv, 64, 128), dtype=torch.int8),
+        v_pool=torch.zeros((n_pages, n_kv, 64, 128), dtype=torch.int8),
+        k_scale=torch.zeros((n_pages, n_kv, 64), dtype=torch.float32),
+        v_scale=torch.zeros((n_pages, n_kv, 64), dtype=torch.float32),
+        page_table=torch.zeros(n_pages, dtype=torch.int32),
+        sel=torch.zeros((n_q, cap), dtype=torch.int32),
+        sel_len=torch.zeros(n_q, dtype=torch.int32),
+        cells=torch.zeros(((n_q + 7) // 8, 8 * cap), dtype=torch.int32),
+        mask=torch.zeros(((n_q + 7) // 8, 8 * cap), dtype=torch.uint8),
+        length=torch.zeros((n_q + 7) // 8, dtype=torch.int32))
+
+
+def test_convenience_outputs_checked_before_the_library(monkeypatch):
+    # Caller-supplied outputs and status words of the wrong dtype or shape
+    # never reach a kernel: the binding raises first (CPU tensors; the C
+    # entry points are replaced by functions that fail the test if called).
+    import torch
+    import sparse_top_selection_amd as sa
+
+    def never(*a, **k):
+        raise AssertionError("reached the library")
+    for name in sa.EXPORTED:
+        if name not in ("sel_attn_last_error", "sel_attn_decode_workspace_bytes"):
+            monkeypatch.setattr(sa, name, never)
+    p = _small_problem()
+    n_ctx = 4 * 64
+    pool = (p["q"], p["k_pool"], p["v_pool"], p["k_scale"], p["v_scale"], p["page_table"])
+    short = torch.zeros((9, 12, 128), dtype=torch.float32)
+    wide_status = torch.zeros(2, dtype=torch.int32)
+    u32_status = torch.zeros(1, dtype=torch.int64)
+
+    cases = [
+        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx, out=short),
+        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+                           out=p["q"].double()),
+        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+                           status=wide_status),
+        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+                           status=u32_status),
+        lambda: sa.prefill_positions(*pool, p["sel"], p["sel_len"], 0.1, n_ctx, out=short),
+        lambda: sa.prefill_positions(*pool, p["sel"], p["sel_len"], 0.1, n_ctx,
+                                     status=wide_status),
+        lambda: sa.decode(*pool, p["sel"], p["sel_len"], 0.1, n_ctx, out=short),
+        lambda: sa.decode(*pool, p["sel"], p["sel_len"], 0.1, n_ctx,
+                          workspace=torch.zeros(64, dtype=torch.int32)),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx,
+                               out=(p["cells"][:1], p["mask"], p["length"])),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx,
+                               out=(p["cells"], p["mask"].to(torch.int8), p["length"])),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx,
+                               out=(p["cells"], p["mask"], p["length"][:1])),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx, status=wide_status),
+        lambda: sa.select_blocks(torch.zeros((10, 4), dtype=torch.float32), 200, n_ctx,
+                                 out=(p["sel"], p["sel_len"][:3])),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises((ValueError, TypeError)):
+            case()
+    # the same calls with valid arguments do reach the library
+    with pytest.raises(AssertionError, match="reached the library"):
+        sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+                   out=torch.zeros_like(p["q"]), status=torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(AssertionError, match="reached the library"):
+        sa.build_union(p["sel"], p["sel_len"], n_ctx,
+                       out=(p["cells"], p["mask"], p["length"]))
