@@ -1,0 +1,54 @@
+"""Host-side logic of bench.py that needs no GPU: the one-GPU refusal, the
+counter summaries' source-hash guard and the recorded command lines."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT,
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stdout + res.stderr
+
+
+def test_counter_traffic_only_for_matching_sources(monkeypatch):
+    for op, workload in (("path", "ctx32k_drift005"), ("select", "ctx32k_drift005"),
+                         ("positions", "ctx64k_independent")):
+        path = os.path.join(ROOT, "profiles", bench._profile_names(workload, op)[1])
+        with open(path) as f:
+            rec = json.load(f)
+        monkeypatch.setattr(bench, "source_hash", lambda o, h=rec["source_hash"]: h)
+        assert bench.counter_traffic(workload, op) == rec["hbm_bytes_per_launch"] > 0
+        monkeypatch.setattr(bench, "source_hash", lambda o: "0" * 16)
+        assert bench.counter_traffic(workload, op) is None
+
+
+def test_source_hash_covers_each_ops_sources():
+    hashes = {op: bench.source_hash(op) for op in bench.OP_SOURCES}
+    assert all(len(h) == 16 for h in hashes.values())
+    assert len({hashes["path"], hashes["select"], hashes["positions"]}) == 3
+    for op, names in bench.OP_SOURCES.items():
+        for name in names:
+            assert os.path.exists(os.path.join(ROOT, "sparse_top_selection_amd", "csrc", name))
+
+
+def test_profile_summaries_name_their_commands():
+    # every committed stats summary records the rocprofv3 command that made it,
+    # and those commands run committed files only
+    pdir = os.path.join(ROOT, "profiles")
+    stats = [n for n in os.listdir(pdir) if n.endswith("_stats.txt")]
+    assert stats
+    for name in stats:
+        text = open(os.path.join(pdir, name)).read()
+        cmds = [l for l in text.splitlines() if l.startswith("command: rocprofv3")]
+        assert cmds, name
+        for c in cmds:
+            assert "_work" not in c and "/root/reference" not in c, c
+            assert "$REPO/bench.py" in c, c
