@@ -189,6 +189,28 @@ def test_attention_empty_groups_and_chunk_remainders():
     assert np.all(out[8:16] == 0) and np.all(out[30] == 0)
 
 
+def test_attention_union_at_full_capacity():
+    """Eight positions with disjoint full selections: the group's union holds
+    8 * 2,051 = 16,408 cells, its row's whole capacity (513 chunks of 32, the
+    last one a quarter full). The last group of the call is such a group, so
+    its union row ends where the union arrays end; the group before it is the
+    same with its rows in random order, and some pages are not resident."""
+    print("case full-capacity union", flush=True)
+    cap = 2051
+    n_ctx = 8 * cap + 700
+    d = synth.small_random(43, n_ctx=n_ctx, n_q=16, n_kv=2, sel_cap=cap, max_len=1,
+                           nonresident_frac=0.1, pool_extra=1)
+    rng = np.random.default_rng(44)
+    sel = np.empty((16, cap), dtype=np.int32)
+    for g in range(2):
+        cells = rng.permutation(n_ctx)[:8 * cap].astype(np.int32).reshape(8, cap)
+        sel[8 * g:8 * g + 8] = cells if g == 0 else np.sort(cells, axis=1)
+    d["sel"], d["sel_len"] = sel, np.full(16, cap, dtype=np.int32)
+    ref_union = oracle.union(d["sel"], d["sel_len"], n_ctx)
+    assert np.all(ref_union[2] == 8 * cap)
+    _check_problem(d, what="full-capacity union")
+
+
 def test_attention_exact_mean_catches_single_cell_errors():
     """k_scale = 0 and v_scale = 2^-6: every logit is exactly 0, so every chosen
     probability is exactly 1 in FP16 and the sums are exact in FP32; the output
