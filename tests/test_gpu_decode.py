@@ -119,3 +119,26 @@ def test_decode_flags_data_errors():
     assert v & sa.STATUS_PAGE_RANGE and v & sa.STATUS_V_SCALE
     assert v & sa.STATUS_CELL_RANGE and v & sa.STATUS_SEL_LEN
     assert np.all(np.isfinite(out.cpu().numpy()))
+
+
+def test_decode_rows_at_the_cap():
+    """Rows of 2,560 entries (the cap, 40 splits): 2,560 distinct cells shuffled
+    (the dedup table at its fullest) or ascending, and 1,280 cells twice each."""
+    print("case decode rows at the cap", flush=True)
+    rng = np.random.default_rng(91)
+    n_ctx = 70000
+    d = synth.small_random(91, n_ctx=n_ctx, n_q=3, n_kv=2, sel_cap=2560, max_len=10,
+                           nonresident_frac=0.1)
+    sel = np.empty((3, 2560), np.int32)
+    for j in range(3):
+        p = n_ctx - 3 + j
+        if j < 2:
+            cells = rng.choice(p + 1, size=2560, replace=False)
+            sel[j] = cells if j == 0 else np.sort(cells)
+        else:
+            cells = rng.choice(p + 1, size=1280, replace=False)
+            sel[j] = rng.permutation(np.concatenate([cells, cells]))
+    d["sel"], d["sel_len"] = sel, np.full(3, 2560, np.int32)
+    out, status = run_decode(d)
+    assert status == 0
+    H.assert_close(out, oracle.attention_of(d), "decode rows at the cap")

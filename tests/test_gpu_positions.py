@@ -75,7 +75,8 @@ def test_positions_random_selections(seed, n_ctx, n_q, n_kv, dup, nonres):
 
 def test_positions_repeats_fill_the_dedup_table():
     """Rows of 2,560 entries (the cap) holding 1,280 distinct cells twice each,
-    or one cell 2,560 times, in shuffled order."""
+    or one cell 2,560 times, in shuffled order; and 2,560 distinct cells,
+    shuffled (the table at its fullest) or ascending (no table)."""
     print("case positions dedup", flush=True)
     rng = np.random.default_rng(61)
     d = synth.small_random(61, n_ctx=70000, n_q=6, n_kv=2, sel_cap=2560, max_len=10)
@@ -85,6 +86,9 @@ def test_positions_repeats_fill_the_dedup_table():
         p = 70000 - 6 + j
         if j == 3:
             sel[j] = rng.integers(0, p + 1)
+        elif j >= 4:
+            cells = rng.choice(p + 1, size=2560, replace=False)
+            sel[j] = cells if j == 4 else np.sort(cells)
         else:
             cells = rng.choice(p + 1, size=1280, replace=False)
             sel[j] = rng.permutation(np.concatenate([cells, cells]))
