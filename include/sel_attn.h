@@ -26,13 +26,15 @@
  * and for decode (one position, or a short speculative verify window), the
  * same attention split over each position's cells:
  *   sel_attn_decode             selections + q + paged INT8 K/V -> output
+ * (sel_attn_decode_noalloc: the same for callers that cannot allocate).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All array pointers are DEVICE pointers owned by the caller. The library
  *   allocates no device memory, keeps no state between calls except a cached
- *   per-device architecture check, and enqueues its kernels asynchronously on
- *   `stream` (NULL = the null stream). Inputs are only read.
+ *   per-device architecture check (and, for sel_attn_decode_noalloc, a static
+ *   device array and its per-device address), and enqueues its kernels
+ *   asynchronously on `stream` (NULL = the null stream). Inputs are only read.
  * - Return value: SEL_ATTN_OK when the kernels were enqueued; a negative code
  *   when nothing was enqueued. sel_attn_last_error() then describes why.
  * - Errors that need the data to detect (a cell out of range, a bad length, a
@@ -79,6 +81,7 @@ extern "C" {
 #define SEL_ATTN_SELECT_MAX_CTX 262144 /* n_ctx limit of sel_attn_select_blocks */
 #define SEL_ATTN_POSITIONS_MAX_CAP 2560  /* sel_cap limit of sel_attn_prefill_positions and decode */
 #define SEL_ATTN_DECODE_MAX_Q 65535      /* n_q limit of sel_attn_decode (one grid dimension) */
+#define SEL_ATTN_DECODE_NOALLOC_MAX_BYTES 8388608 /* static scratch of sel_attn_decode_noalloc (8 MiB) */
 
 typedef struct sel_attn_dims {
   int32_t n_ctx;     /* logical context length in cells, >= 1; page_table has
@@ -254,6 +257,33 @@ int sel_attn_decode(const sel_attn_dims* d, const float* q, const int8_t* k_pool
                     const int32_t* page_table, const int32_t* sel, const int32_t* sel_len,
                     float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
                     uint32_t* status, hipStream_t stream);
+
+/*
+ * sel_attn_decode_noalloc - sel_attn_decode for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. It allocates nothing and
+ * calls no allocating routine; the split records go to a static device array
+ * of SEL_ATTN_DECODE_NOALLOC_MAX_BYTES that the library holds on every GPU it
+ * runs on until the process ends (its address is looked up once per device,
+ * on the first call there).
+ *
+ *   arguments as for sel_attn_decode, without the workspace
+ *   The caller still provides q, the pools, scales, page table, selections,
+ *   out and status. Outputs are bitwise identical to sel_attn_decode's for the
+ *   same inputs (same kernels). Every call on one GPU shares that GPU's array
+ *   and finds it as the last call left it (nothing in it has to start at
+ *   zero): calls that overlap on one GPU (different streams, or several host
+ *   threads) race and must be serialised by the caller.
+ *   Errors: as sel_attn_decode; dims whose split records exceed the array
+ *   (sel_attn_decode_workspace_bytes(d) > SEL_ATTN_DECODE_NOALLOC_MAX_BYTES,
+ *   e.g. more than 8 positions x 4 KV heads at sel_cap 2,560) give EINVAL
+ *   with nothing enqueued.
+ */
+int sel_attn_decode_noalloc(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                            const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                            const int32_t* page_table, const int32_t* sel, const int32_t* sel_len,
+                            float softmax_scale, float* out, uint32_t* status,
+                            hipStream_t stream);
 
 /*
  * sel_attn_last_error - text describing the last nonzero return of an entry

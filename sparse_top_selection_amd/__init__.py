@@ -54,10 +54,11 @@ SEL_MAX = 2051
 SELECT_MAX_CTX = 262144
 POSITIONS_MAX_CAP = 2560
 DECODE_MAX_Q = 65535
+DECODE_NOALLOC_MAX_BYTES = 8388608
 
 EXPORTED = ("sel_attn_select_blocks", "sel_attn_build_union", "sel_attn_prefill",
             "sel_attn_prefill_positions", "sel_attn_decode_workspace_bytes", "sel_attn_decode",
-            "sel_attn_last_error")
+            "sel_attn_decode_noalloc", "sel_attn_last_error")
 
 
 class Dims(ctypes.Structure):
@@ -89,6 +90,9 @@ _lib.sel_attn_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.sel_attn_decode.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
                                  ctypes.c_float, _p, _p, ctypes.c_size_t, _p, _p]
 _lib.sel_attn_decode.restype = ctypes.c_int
+_lib.sel_attn_decode_noalloc.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
+                                         ctypes.c_float, _p, _p, _p]
+_lib.sel_attn_decode_noalloc.restype = ctypes.c_int
 _lib.sel_attn_last_error.argtypes = []
 _lib.sel_attn_last_error.restype = ctypes.c_char_p
 
@@ -174,6 +178,16 @@ def sel_attn_decode(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table,
                                 _ptr(sel_len), ctypes.c_float(float(softmax_scale)), _ptr(out),
                                 _ptr(workspace), int(workspace_bytes), _ptr(status),
                                 _stream(stream)))
+
+
+def sel_attn_decode_noalloc(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel,
+                            sel_len, softmax_scale: float, out, status, stream=None) -> None:
+    """Enqueue the decode attention with the library's static scratch instead of
+    a workspace (see include/sel_attn.h). Tensors or raw device pointers."""
+    _check(_lib.sel_attn_decode_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        _ptr(k_scale), _ptr(v_scale), _ptr(page_table), _ptr(sel),
+                                        _ptr(sel_len), ctypes.c_float(float(softmax_scale)),
+                                        _ptr(out), _ptr(status), _stream(stream)))
 
 
 # --------------------------------------------------------------------------

@@ -326,3 +326,81 @@ int sel_attn_decode(const sel_attn_dims* d, const float* q, const int8_t* k_pool
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The decode call without a caller workspace. Its split records live in
+// `scratch`, a file-scope device array that every GPU the library runs on
+// holds until the process ends. In host code the name `scratch` is only a
+// host-side stand-in for that array, so its device address is taken once per
+// device with hipGetSymbolAddress (with that device current) and only that
+// address is ever handed to a kernel.
+__device__ __align__(256) unsigned char scratch[SEL_ATTN_DECODE_NOALLOC_MAX_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up on the first
+// call that runs on it. Returns SEL_ATTN_OK or ELAUNCH.
+int scratch_address(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SEL_ATTN_EUNSUPPORTED, "%s: device ordinal %d", who, dev);
+  static std::mutex mu;
+  static void* ptr[64];
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SEL_ATTN_ELAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d: %s", who, dev,
+                  hipGetErrorString(e));
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return SEL_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sel_attn_decode_noalloc(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                            const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                            const int32_t* page_table, const int32_t* sel, const int32_t* sel_len,
+                            float softmax_scale, float* out, uint32_t* status,
+                            hipStream_t stream) {
+  static const char* who = "sel_attn_decode_noalloc";
+  int rc = check_dims(d, who);
+  if (rc) return rc;
+  if (d->n_q > 0) {
+    const size_t need = sel_attn_decode_workspace_bytes(d);
+    if (need > (size_t)SEL_ATTN_DECODE_NOALLOC_MAX_BYTES)
+      return fail(SEL_ATTN_EINVAL,
+                  "%s: these dims need %zu bytes of split records, above the %d-byte static "
+                  "scratch (n_q * n_kv * ceil(sel_cap / 64) must stay <= %d); use sel_attn_decode "
+                  "with a workspace",
+                  who, need, SEL_ATTN_DECODE_NOALLOC_MAX_BYTES,
+                  (int)(SEL_ATTN_DECODE_NOALLOC_MAX_BYTES / sizeof(selattn::DecodePartial)));
+    if (d->n_q > SEL_ATTN_DECODE_MAX_Q)
+      return fail(SEL_ATTN_EINVAL, "%s: n_q %d above %d", who, d->n_q, SEL_ATTN_DECODE_MAX_Q);
+  }
+  selattn::PositionsArgs a;
+  rc = positions_args(d, who, q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
+                      softmax_scale, out, status, a);
+  if (rc) return rc;
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
+  void* ws = nullptr;
+  rc = scratch_address(who, &ws);
+  if (rc) return rc;
+  // every record the merge reads is written by the split kernel of the same
+  // call, so nothing in the scratch needs clearing between calls
+  hipError_t e = selattn::launch_decode(a, static_cast<selattn::DecodePartial*>(ws), stream);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SEL_ATTN_OK;
+}
+
+}  // extern "C"

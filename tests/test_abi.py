@@ -19,6 +19,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["sel_attn_build_union", "sel_attn_decode",
+                                    "sel_attn_decode_noalloc",
                                     "sel_attn_decode_workspace_bytes", "sel_attn_last_error",
                                     "sel_attn_prefill", "sel_attn_prefill_positions",
                                     "sel_attn_select_blocks"]
@@ -131,6 +132,29 @@ def test_decode_rejects_on_host():
         sa.sel_attn_decode(_dims(sel_cap=2561), *args, 0.1, FAKE, FAKE, 1 << 30, FAKE, stream=0)
     assert e.value.code == -2
     sa.sel_attn_decode(_dims(n_q=0), *(None,) * 8, 0.1, None, None, 0, FAKE, stream=0)
+    assert sa.sel_attn_last_error() == ""
+
+
+def test_decode_noalloc_rejects_on_host():
+    """The allocation-free decode refuses dims whose split records exceed its
+    static array, and bad arguments, before touching the device."""
+    import sparse_top_selection_amd as sa
+    args = (FAKE,) * 8
+    for n_q, n_kv, cap in ((9, 4, 2560), (1, 34, 2560), (11, 4, 2051)):
+        d = _dims(n_q=n_q, n_kv=n_kv, sel_cap=cap, n_pages=16)
+        assert sa.sel_attn_decode_workspace_bytes(d) > sa.DECODE_NOALLOC_MAX_BYTES
+        with pytest.raises(sa.SelAttnError) as e:
+            sa.sel_attn_decode_noalloc(d, *args, 0.1, FAKE, FAKE, stream=0)
+        assert e.value.code == -1 and "static scratch" in sa.sel_attn_last_error()
+    ok = _dims(n_q=8, n_kv=4, sel_cap=2560)
+    assert sa.sel_attn_decode_workspace_bytes(ok) <= sa.DECODE_NOALLOC_MAX_BYTES
+    with pytest.raises(sa.SelAttnError) as e:   # fits, but a NULL array pointer
+        sa.sel_attn_decode_noalloc(ok, *args[:7], None, 0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -1 and "NULL" in sa.sel_attn_last_error()
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_decode_noalloc(_dims(sel_cap=2561), *args, 0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -2
+    sa.sel_attn_decode_noalloc(_dims(n_q=0), *(None,) * 8, 0.1, None, FAKE, stream=0)
     assert sa.sel_attn_last_error() == ""
 
 
