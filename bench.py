@@ -323,7 +323,7 @@ def main():
     mask = torch.empty((g, 8 * cap), dtype=torch.uint8, device=dev)
     length = torch.empty(g, dtype=torch.int32, device=dev)
     out = torch.empty_like(t["q"])
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    status = sa.new_status(dev)
     dims = sa.make_dims(w.n_ctx, w.n_q, w.n_kv, w.pool_pages, sel_cap=cap)
     scale = float(inp["softmax_scale"])
     stream = torch.cuda.current_stream(dev)
@@ -494,7 +494,7 @@ def bench_decode(args):
     t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
          for k in ("q", "k_pool", "v_pool", "k_scale", "v_scale", "page_table", "sel", "sel_len")}
     out = torch.empty_like(t["q"])
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    status = sa.new_status(dev)
     dims = sa.make_dims(w.n_ctx, nd, w.n_kv, w.pool_pages, sel_cap=w.sel_cap)
     ws_bytes = sa.sel_attn_decode_workspace_bytes(dims)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

@@ -193,6 +193,16 @@ def sel_attn_decode_noalloc(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, pag
 # --------------------------------------------------------------------------
 # conveniences over torch tensors
 # --------------------------------------------------------------------------
+def _on_gpu(t: torch.Tensor, name: str) -> torch.device:
+    """The tensor's device, which must be a GPU: the kernels dereference every
+    pointer they are given, so a host tensor must never reach them."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU (got %s)" % (name, t.device))
+    return t.device
+
+
 def _need(t: torch.Tensor, name: str, dtype, ndim: int, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
@@ -216,17 +226,25 @@ def _need_shape(t, name: str, dtype, shape, device):
 def _status_for(status, device) -> torch.Tensor:
     if status is None:
         return new_status(device)
-    _need_shape(status, "status", torch.int32, (1,), device)
+    _need_shape(status, "status", torch.uint32, (1,), device)
     return status
 
 
 def new_status(device) -> torch.Tensor:
-    return torch.zeros(1, dtype=torch.int32, device=device)
+    """A zeroed status word: uint32 [1] on the device, as the header declares it
+    (filled as int32 zeros and viewed as uint32: same bytes, no uint32 kernel)."""
+    return torch.zeros(1, dtype=torch.int32, device=device).view(torch.uint32)
+
+
+def status_value(status: torch.Tensor) -> int:
+    """Synchronise on a status word and return its bits as an unsigned int
+    (read through an int32 view of the same 4 bytes)."""
+    return int(status.view(torch.int32).item()) & 0xFFFFFFFF
 
 
 def check_status(status: torch.Tensor) -> int:
     """Synchronise on the status word and raise on any set bit."""
-    v = int(status.item()) & 0xFFFFFFFF
+    v = status_value(status)
     if v:
         names = [n for n, b in (("CELL_RANGE", 1), ("SEL_LEN", 2), ("PAGE_RANGE", 4),
                                 ("UNION_LEN", 8), ("V_SCALE", 16)) if v & b]
@@ -239,8 +257,8 @@ def select_blocks(block_scores: torch.Tensor, first_pos: int, n_ctx: int,
     """Selections of positions first_pos .. first_pos + n_q - 1 from block
     scores float32 [n_q][ceil(n_ctx/64)]. Returns (sel, sel_len); entries past
     sel_len are left as allocated (torch.empty) or as they were in `out`."""
-    dev = block_scores.device
-    _need(block_scores, "block_scores", torch.float32, 2, None)
+    dev = _on_gpu(block_scores, "block_scores")
+    _need(block_scores, "block_scores", torch.float32, 2, dev)
     n_q, nb = block_scores.shape
     if nb != -(-n_ctx // PAGE_SIZE):
         raise ValueError("block_scores must be [n_q][ceil(n_ctx/64)]")
@@ -262,8 +280,8 @@ def select_blocks(block_scores: torch.Tensor, first_pos: int, n_ctx: int,
 def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, status=None, stream=None,
                 out=None):
     """Union of every group of 8 query indices. Returns (cells, mask, length, status)."""
-    dev = sel.device
-    _need(sel, "sel", torch.int32, 2, None)
+    dev = _on_gpu(sel, "sel")
+    _need(sel, "sel", torch.int32, 2, dev)
     _need(sel_len, "sel_len", torch.int32, 1, dev)
     n_q, cap = sel.shape
     if sel_len.shape[0] != n_q:
@@ -287,8 +305,8 @@ def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, status=Non
 def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_mask, union_len,
             softmax_scale: float, n_ctx: int, status=None, stream=None, out=None):
     """Attention over each group's union. Returns (out, status)."""
-    dev = q.device
-    _need(q, "q", torch.float32, 3, None)
+    dev = _on_gpu(q, "q")
+    _need(q, "q", torch.float32, 3, dev)
     for name, t, dt, nd in (("k_pool", k_pool, torch.int8, 4), ("v_pool", v_pool, torch.int8, 4),
                             ("k_scale", k_scale, torch.float32, 3),
                             ("v_scale", v_scale, torch.float32, 3),
@@ -323,8 +341,8 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
 
 
 def _positions_dims(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, n_ctx):
-    dev = q.device
-    _need(q, "q", torch.float32, 3, None)
+    dev = _on_gpu(q, "q")
+    _need(q, "q", torch.float32, 3, dev)
     for name, t, dt, nd in (("k_pool", k_pool, torch.int8, 4), ("v_pool", v_pool, torch.int8, 4),
                             ("k_scale", k_scale, torch.float32, 3),
                             ("v_scale", v_scale, torch.float32, 3),

@@ -29,7 +29,7 @@ def run_path(problem: dict, dev: dict = None):
         int(problem["n_ctx"]))
     torch.cuda.synchronize()
     return (out.cpu().numpy(), cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
-            int(status.item()) & 0xFFFFFFFF)
+            sa.status_value(status))
 
 
 def assert_union_equal(cells, mask, length, ref):

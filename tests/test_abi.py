@@ -231,6 +231,10 @@ def test_convenience_outputs_checked_before_the_library(monkeypatch):
     for name in sa.EXPORTED:
         if name not in ("sel_attn_last_error", "sel_attn_decode_workspace_bytes"):
             monkeypatch.setattr(sa, name, never)
+    # these CPU tensors stand in for GPU ones: only the shape and dtype checks
+    # are under test here (test_host_tensors_never_reach_the_library covers
+    # the device check)
+    monkeypatch.setattr(sa, "_on_gpu", lambda t, name: t.device)
     p = _small_problem()
     n_ctx = 4 * 64
     pool = (p["q"], p["k_pool"], p["v_pool"], p["k_scale"], p["v_scale"], p["page_table"])
@@ -268,7 +272,43 @@ def test_convenience_outputs_checked_before_the_library(monkeypatch):
     # the same calls with valid arguments do reach the library
     with pytest.raises(AssertionError, match="reached the library"):
         sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
-                   out=torch.zeros_like(p["q"]), status=torch.zeros(1, dtype=torch.int32))
+                   out=torch.zeros_like(p["q"]), status=torch.zeros(1, dtype=torch.uint32))
     with pytest.raises(AssertionError, match="reached the library"):
         sa.build_union(p["sel"], p["sel_len"], n_ctx,
                        out=(p["cells"], p["mask"], p["length"]))
+
+
+def test_host_tensors_never_reach_the_library(monkeypatch):
+    """Every convenience refuses tensors that are not on a GPU before any C
+    entry point is called: a kernel handed host pointers would fault."""
+    import torch
+    import sparse_top_selection_amd as sa
+
+    def never(*a, **k):
+        raise AssertionError("reached the library")
+    for name in sa.EXPORTED:
+        if name not in ("sel_attn_last_error", "sel_attn_decode_workspace_bytes"):
+            monkeypatch.setattr(sa, name, never)
+    p = _small_problem()
+    n_ctx = 4 * 64
+    pool = (p["q"], p["k_pool"], p["v_pool"], p["k_scale"], p["v_scale"], p["page_table"])
+    cases = [
+        lambda: sa.select_blocks(torch.zeros((10, 4), dtype=torch.float32), 200, n_ctx),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx),
+        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx),
+        lambda: sa.prefill_positions(*pool, p["sel"], p["sel_len"], 0.1, n_ctx),
+        lambda: sa.decode(*pool, p["sel"], p["sel_len"], 0.1, n_ctx),
+        lambda: sa.attention(*pool, p["sel"], p["sel_len"], 0.1, n_ctx),
+    ]
+    for case in cases:
+        with pytest.raises(ValueError, match="must be on a GPU"):
+            case()
+
+
+def test_status_word_is_the_headers_uint32():
+    """new_status() gives the header's status type: one zeroed uint32."""
+    import torch
+    import sparse_top_selection_amd as sa
+    st = sa.new_status(torch.device("cpu"))
+    assert st.dtype == torch.uint32 and tuple(st.shape) == (1,) and sa.status_value(st) == 0
+    assert sa.check_status(st) == 0

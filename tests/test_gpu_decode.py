@@ -46,7 +46,7 @@ def run_decode(d: dict, dev: dict = None, workspace=None):
                             dev["v_scale"], dev["page_table"], dev["sel"], dev["sel_len"],
                             float(d["softmax_scale"]), int(d["n_ctx"]), workspace=workspace)
     torch.cuda.synchronize()
-    return out.cpu().numpy(), int(status.item()) & 0xFFFFFFFF
+    return out.cpu().numpy(), sa.status_value(status)
 
 
 @pytest.mark.parametrize("idx,n", [(0, 1), (1, 1), (2, 1), (3, 5), (4, 1), (4, 5), (2, 8)])
@@ -115,7 +115,7 @@ def test_decode_flags_data_errors():
     out, st = sa.decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], vs, pt, sel,
                         sel_len, float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
-    v = int(st.item())
+    v = sa.status_value(st)
     assert v & sa.STATUS_PAGE_RANGE and v & sa.STATUS_V_SCALE
     assert v & sa.STATUS_CELL_RANGE and v & sa.STATUS_SEL_LEN
     assert np.all(np.isfinite(out.cpu().numpy()))

@@ -7,6 +7,8 @@ groups, long contexts (several union windows) and a bitwise rerun.
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
 section Accuracy (the parity self-test's cases).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -40,7 +42,7 @@ def test_union_bit_exact_on_workloads(idx):
     sel_len = torch.from_numpy(d["sel_len"]).cuda()
     cells, mask, length, status = sa.build_union(sel, sel_len, w.n_ctx)
     torch.cuda.synchronize()
-    assert int(status.item()) == 0
+    assert sa.status_value(status) == 0
     H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
                          oracle.union(d["sel"], d["sel_len"], w.n_ctx))
 
@@ -68,7 +70,7 @@ def test_union_bit_exact_edge_cases(n_ctx, n_q, seed):
     cells, mask, length, status = sa.build_union(torch.from_numpy(sel).cuda(),
                                                  torch.from_numpy(sel_len).cuda(), n_ctx)
     torch.cuda.synchronize()
-    assert int(status.item()) == 0
+    assert sa.status_value(status) == 0
     H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
                          oracle.union(sel, sel_len, n_ctx))
 
@@ -94,7 +96,7 @@ def test_union_bit_exact_any_row_stride_and_alignment(n_ctx, n_q, cap, offset, s
     assert dev.data_ptr() % 16 != 0
     cells, mask, length, status = sa.build_union(dev, torch.from_numpy(sel_len).cuda(), n_ctx)
     torch.cuda.synchronize()
-    assert int(status.item()) == 0
+    assert sa.status_value(status) == 0
     H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
                          oracle.union(sel, sel_len, n_ctx))
 
@@ -109,7 +111,7 @@ def test_union_flags_bad_cells_and_lengths():
     cells, mask, length, status = sa.build_union(torch.from_numpy(sel).cuda(),
                                                  torch.from_numpy(sel_len).cuda(), 100)
     torch.cuda.synchronize()
-    st = int(status.item())
+    st = sa.status_value(status)
     assert st & sa.STATUS_CELL_RANGE and st & sa.STATUS_SEL_LEN
     # the bad cells are dropped, the rest of the group is intact
     assert length.cpu().tolist()[0] == 3
@@ -145,6 +147,16 @@ def test_attention_workloads_all_rows(idx):
     # a property that holds for every output: a convex combination of V rows
     vmax = float(np.abs(d["v_pool"].astype(np.float32) * d["v_scale"][..., None]).max())
     assert float(np.abs(out).max()) <= vmax * (1 + 1e-2)
+
+
+@pytest.mark.parametrize("seed", [2004, 3004])
+def test_attention_independent_workload_other_seeds(seed):
+    """The 64K workload (independent selections, scales up to 0.05) has the
+    largest error against FP64; two more draws of all its inputs, every output
+    checked, so that the margin to the gate is not the luck of one seed."""
+    w = dataclasses.replace(synth.workload(4), seed=seed)
+    print("case", w.name, "seed", seed, flush=True)
+    _check_problem(synth.as_problem(synth.generate(w)), what="%s seed %d" % (w.name, seed))
 
 
 @pytest.mark.parametrize("seed,n_ctx,n_q,n_kv,dup,nonres", [
@@ -270,7 +282,7 @@ def test_attention_flags_data_errors():
     dev = H.to_device(d)
     cells, mask, length, status = sa.build_union(dev["sel"], dev["sel_len"], 640)
     torch.cuda.synchronize()
-    assert int(status.item()) == 0
+    assert sa.status_value(status) == 0
     # a page-table entry past the pool and a too-large v_scale
     pt = dev["page_table"].clone()
     pt[2] = d["n_pages"] + 5
@@ -279,7 +291,7 @@ def test_attention_flags_data_errors():
     out, st = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], vs, pt, cells,
                          mask, length, float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
-    v = int(st.item())
+    v = sa.status_value(st)
     assert v & sa.STATUS_PAGE_RANGE and v & sa.STATUS_V_SCALE
     # a union length over the capacity is clamped and flagged
     bad_len = length.clone()
@@ -288,7 +300,7 @@ def test_attention_flags_data_errors():
                          dev["v_scale"], dev["page_table"], cells, mask, bad_len,
                          float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
-    assert int(st.item()) & sa.STATUS_UNION_LEN
+    assert sa.status_value(st) & sa.STATUS_UNION_LEN
 
 
 # ------------------------------------------------ residency stress and replayed selections

@@ -39,7 +39,7 @@ def run_positions(d: dict, dev: dict = None):
                                        dev["v_scale"], dev["page_table"], dev["sel"],
                                        dev["sel_len"], float(d["softmax_scale"]), int(d["n_ctx"]))
     torch.cuda.synchronize()
-    return out.cpu().numpy(), int(status.item()) & 0xFFFFFFFF
+    return out.cpu().numpy(), sa.status_value(status)
 
 
 def _check(d, rows=None, what=""):
@@ -151,7 +151,7 @@ def test_positions_flags_data_errors():
     out, st = sa.prefill_positions(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], vs, pt,
                                    sel, sel_len, float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
-    v = int(st.item())
+    v = sa.status_value(st)
     assert v & sa.STATUS_PAGE_RANGE and v & sa.STATUS_V_SCALE
     assert v & sa.STATUS_CELL_RANGE and v & sa.STATUS_SEL_LEN
     assert np.all(np.isfinite(out.cpu().numpy()))

@@ -68,8 +68,8 @@ def both_calls(d: dict):
                        dev["v_scale"], dev["page_table"], dev["sel"], dev["sel_len"], scale, out_b,
                        ws, need, st_b)
     torch.cuda.synchronize()
-    assert int(st_b.item()) == 0
-    return out_a.cpu().numpy(), out_b.cpu().numpy(), int(st_a.item()) & 0xFFFFFFFF
+    assert sa.status_value(st_b) == 0
+    return out_a.cpu().numpy(), out_b.cpu().numpy(), sa.status_value(st_a)
 
 
 def check_case(d: dict, what: str):
