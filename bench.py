@@ -37,7 +37,8 @@ F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix
 #   K row 128 + V row 128 + k_scale 4 + v_scale 4 (the union K/V bytes: 264)
 #   + union cell index 4 + chooser byte 1 + page-table entry 4
 UNION_KV_BYTES = 264
-UNION_CELL_BYTES = UNION_KV_BYTES + 4 + 1 + 4
+UNION_CELL_BYTES = UNION_KV_BYTES + 4 + 1   # + union cell index and chooser byte
+RIDGE_FLOP_PER_BYTE = F16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROW_BYTES = 128 * 4 * 2        # q in + out, per (query position, query head)
 FLOP_PER_CELL_ROW = 4 * 128    # QK^T and PV, per (union cell, row)
 SELECT_RHO = 0.99              # AR(1) correlation of the block scores across positions
@@ -71,6 +72,17 @@ def parse():
     ap.add_argument("--sel", metavar="FILE",
                     help="replay recorded selections (.npz from synth.save_selections) instead of "
                          "the workload's own; n_ctx and n_q come from the file")
+    ap.add_argument("--ctx", type=int, default=None, metavar="N",
+                    help="timing mode: a workload of N context cells built from the arguments "
+                         "(with --queries and --drift; the last Q positions, 4 KV heads) instead "
+                         "of a named one")
+    ap.add_argument("--queries", type=int, default=8192, metavar="Q",
+                    help="timing mode: query positions (the last Q of the context)")
+    ap.add_argument("--drift", type=float, default=0.05, metavar="F",
+                    help="timing mode: share of far-block choices redrawn from one position to "
+                         "the next (1.0 = independent selections)")
+    ap.add_argument("--kv-heads", type=int, default=4, metavar="H", help="timing mode: KV heads")
+    ap.add_argument("--seed", type=int, default=2000, help="timing mode: input seed")
     ap.add_argument("--kv-resident", type=float, default=1.0, metavar="F",
                     help="fraction of logical pages resident; the rest are marked -1 (seeded)")
     ap.add_argument("--cpu-rows", type=int, default=-1,
@@ -120,9 +132,9 @@ def _profile_names(workload: str, op: str):
     return "kernels_%s_%s_stats.txt" % (op, workload), "%s_%s_counters.json" % (op, workload)
 
 
-def counter_traffic(workload_name: str, op: str = "path"):
-    """HBM bytes per launch of the op's main kernel from the committed counter
-    summary, if it was taken on the current kernel sources; else None."""
+def counter_record(workload_name: str, op: str = "path"):
+    """The committed counter summary of the op on this workload, if it was taken
+    on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", _profile_names(workload_name, op)[1])
     if not os.path.exists(path):
         return None
@@ -130,7 +142,35 @@ def counter_traffic(workload_name: str, op: str = "path"):
         rec = json.load(f)
     if rec.get("source_hash") != source_hash(op):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def counter_traffic(workload_name: str, op: str = "path"):
+    """HBM bytes per launch of the op's main kernel from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    rec = counter_record(workload_name, op)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def measured_limiter(rec, kernel: str, alg_bytes: float):
+    """What the counters say bounds the kernel: HBM traffic against its
+    algorithmic bytes, and how busy the matrix cores were."""
+    if rec is None:
+        return None
+    traffic = rec["kernels"][kernel]["hbm_bytes"]
+    out = {"hbm_traffic_over_algorithmic_bytes": traffic / alg_bytes}
+    sq = rec.get("sq", {}).get(kernel)
+    if sq:
+        d = sq["derived"]
+        out["matrix_core_busy_frac"] = d.get("matrix-core busy / (4 x CU busy cycles)")
+        out["valu_beside_matrix_core_frac"] = d.get("VALU beside matrix core / matrix-core busy")
+    if out["hbm_traffic_over_algorithmic_bytes"] < 0.5:
+        out["verdict"] = ("cache-fed: HBM carries %.2fx the algorithmic bytes, so the kernel is bound by "
+                          "instruction issue on the CUs (VALU, LDS and MFMA together), not by HBM"
+                          % out["hbm_traffic_over_algorithmic_bytes"])
+    else:
+        out["verdict"] = "HBM traffic near the algorithmic bytes: bandwidth-bound"
+    return out
 
 
 COPY_BYTES = 512 << 20         # the calibration copy of --profile: bytes read, and bytes written
@@ -265,6 +305,21 @@ def summarize(d: str, workload: str, op: str = "path"):
     print(json.dumps(rec, indent=1))
 
 
+def timing_workload(args):
+    """The workload of the timing mode: the 32K chunk's recipe (INT8 pools with
+    per-cell scales behind a shuffled page table, 3 sinks + own block + 31 far
+    blocks) at the context, position count, drift and KV-head count given."""
+    import synth
+    if not (0 < args.queries <= args.ctx):
+        raise SystemExit("--queries must be in [1, --ctx]")
+    if not (0.0 <= args.drift <= 1.0):
+        raise SystemExit("--drift must be in [0, 1]")
+    name = "ctx%d_q%d_drift%g_kv%d" % (args.ctx, args.queries, args.drift, args.kv_heads)
+    return dataclasses.replace(synth.workload(synth.HEADLINE), name=name, n_ctx=args.ctx,
+                               n_q=args.queries, n_kv=args.kv_heads, drift=args.drift,
+                               seed=args.seed, n_pages=None)
+
+
 def main():
     args = parse()
     if args.workload is None:
@@ -291,7 +346,7 @@ def main():
         bench_decode(args)
         return
     dev = torch.device("cuda:0")
-    w = synth.workload(args.workload)
+    w = timing_workload(args) if args.ctx else synth.workload(args.workload)
     label = w.name
     if args.sel:
         rec = synth.load_selections(args.sel)
@@ -379,9 +434,50 @@ def main():
         alg_bytes = union_cells * w.n_kv * UNION_CELL_BYTES + w.n_q * w.n_qh * ROW_BYTES
         kv_bytes = union_cells * w.n_kv * UNION_KV_BYTES
         flops = union_cells * w.n_kv * 96 * FLOP_PER_CELL_ROW
-    achieved = alg_bytes / (prefill_ms * 1e-3) / 1e9
+    sec = prefill_ms * 1e-3
     # the committed counters were taken on the workload's own inputs
-    traffic = None if (args.sel or args.kv_resident < 1.0) else counter_traffic(w.name, args.op)
+    custom = bool(args.sel or args.kv_resident < 1.0 or args.ctx)
+    rec = None if custom else counter_record(w.name, args.op)
+    kernel = "prefill_positions_kernel" if positions else "sel_attn_prefill_kernel"
+    traffic = None if rec is None else rec["kernels"][kernel]["hbm_bytes"]
+    kv_gbps = kv_bytes / sec / 1e9
+    if positions:
+        # The gathered rows (every listed cell of every position) are mostly
+        # re-reads that the L2 and the last-level cache serve, so their rate
+        # exceeds what HBM alone delivers; the roofline line is stated on the
+        # bytes HBM actually carried (counters), which it can meet.
+        roofline = {
+            "kernel": kernel, "bound": "hbm",
+            "basis": "HBM bytes per launch from the FETCH_SIZE / WRITE_SIZE counters",
+            "achieved": None if traffic is None else traffic / sec / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": None if traffic is None else traffic / sec / 1e9 / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "gathered_bytes": {"bytes_per_launch": alg_bytes, "effective_GBps": alg_bytes / sec / 1e9,
+                               "note": "every gathered row counted; most are cache hits"},
+        }
+    else:
+        intensity = flops / kv_bytes
+        roofline = {
+            "kernel": kernel,
+            # by arithmetic intensity against the MI355X ridge (2.5 PFLOP/s / 8 TB/s)
+            "bound": "hbm" if intensity < RIDGE_FLOP_PER_BYTE else "mfma",
+            "basis": "union K/V bytes: 264 B per union cell and KV head (K and V rows, two fp32 scales)",
+            "achieved": kv_gbps, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": kv_gbps / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "intensity_flop_per_byte": intensity,
+            "ridge_flop_per_byte": RIDGE_FLOP_PER_BYTE,
+            "with_indices_and_q_out": {
+                "basis": "+ 5 B of union index and chooser byte per union cell and KV head, "
+                         "+ 98,304 B of q in and out per work-group",
+                "bytes_per_launch": alg_bytes, "achieved": alg_bytes / sec / 1e9,
+                "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS},
+            "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": F16_MFMA_PEAK_TFLOPS,
+                     "frac": flops / sec / 1e12 / F16_MFMA_PEAK_TFLOPS},
+            "measured_limiter": measured_limiter(rec, kernel, kv_bytes),
+        }
 
     if args.profile:
         # plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
@@ -391,10 +487,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    kernel = "prefill_positions_kernel" if positions else "sel_attn_prefill_kernel"
     result = {
         "metric": ("selected query-head-cells/s (per-position attention, %s)" % w.name if positions
-                   else "selected query-head-cells/s (32K-context prompt chunk)"),
+                   else "selected query-head-cells/s (32K-context prompt chunk)"
+                   if w.name == synth.workload(synth.HEADLINE).name
+                   else "selected query-head-cells/s (%s)" % w.name),
         "value": q_head_cells / (ms_per_step * 1e-3),
         "unit": "query-head-cells/s",
         "n_gpus": 1,
@@ -416,19 +513,10 @@ def main():
         "prompt_positions_per_s": w.n_q / (ms_per_step * 1e-3),
         "kernels_ms": ({"prefill_positions": prefill_ms} if positions
                        else {"union_build": union_ms, "prefill": prefill_ms}),
-        "kv_GBps": kv_bytes / (prefill_ms * 1e-3) / 1e9,
-        "kv_frac_of_hbm_peak": kv_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "mfma_frac_of_f16_peak": flops / (prefill_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS,
-        "roofline": {
-            "kernel": kernel,
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg_bytes,
-        },
+        "kv_GBps": kv_gbps,
+        "kv_frac_of_hbm_peak": kv_gbps / HBM_PEAK_GBS,
+        "mfma_frac_of_f16_peak": flops / sec / 1e12 / F16_MFMA_PEAK_TFLOPS,
+        "roofline": roofline,
         "source_hash": source_hash(args.op),
     }
     if not positions:
