@@ -103,7 +103,8 @@ typedef struct sel_attn_dims {
 /*
  * sel_attn_select_blocks - the selection step before the path (section What
  * changed: the selection, block scores then top-k, which the page leaves as it
- * is; section Accuracy: a selection holds at most 2,051 cells). The page does
+ * is; the accuracy list in section Summary: a selection holds at most 2,051
+ * cells). The page does
  * not say how blocks are scored; the scores are an input.
  *
  *   first_pos     position of query index 0; query index j is at position
@@ -128,10 +129,10 @@ int sel_attn_select_blocks(const sel_attn_dims* d, int32_t first_pos, const floa
                            int32_t* sel, int32_t* sel_len, hipStream_t stream);
 
 /*
- * sel_attn_build_union - the union step (section Summary: a first kernel builds,
- * for every 8 neighbouring positions, the sorted union of their selected cells,
- * marking each cell with the positions that chose it; section What changed:
- * one work-group per 8 positions with local bitmaps).
+ * sel_attn_build_union - the union step (section Summary: per group of 8
+ * adjacent positions, one sorted list of every cell any of them selected, each
+ * entry tagged with which of the 8 selected it; section What changed: one
+ * work-group per 8 positions with local bitmaps).
  *
  *   sel          const int32 [n_q][sel_cap]   selected logical cells of each
  *                                             query index; any order, repeats
@@ -181,8 +182,8 @@ int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32
  *                                                       resident cells; 0 when
  *                                                       it has none
  *   status       uint32 [1]                             in/out, as above
- *   Precision: Q, dequantised K, V and the probabilities enter the products as
- *   FP16 (round to nearest even); scores, softmax and sums are FP32. K and V
+ *   Precision: both matrix products take their operands (Q, dequantised K, V
+ *   and the probabilities) in FP16 (round to nearest even); scores, softmax and sums are FP32. K and V
  *   integers are exact in FP16; k_scale is applied to the FP32 score, v_scale
  *   as an FP16 factor (v_scale * 2^6) on the FP16 probability.
  *   Supported scales: |v_scale| < 4 (other values set V_SCALE); k_scale any
@@ -202,14 +203,14 @@ int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_poo
  * sel_attn_prefill, computed per position with no union: every position
  * gathers its own selected cells (section Summary: the FP32 kernel in which
  * every position gathers its own ~2,051 cells defines what is computed;
- * section Extra Notes: the union kernel pays only when neighbouring selections
- * overlap, and with independent selections it is no faster). Pick this call
+ * section Extra Notes: the union path wins only where adjacent positions'
+ * selections share cells, and gains nothing when they are unrelated). Pick this call
  * when the union of 8 neighbours is several times one selection.
  *
  *   q, k_pool, v_pool, k_scale, v_scale, page_table, softmax_scale, out,
  *   status      as for sel_attn_prefill
  *   sel, sel_len as for sel_attn_build_union: any order, repeats count once
- *   Precision: Q, K, V and P' = p * v_scale * 2^6 enter the products as FP16
+ *   Precision: the products take Q, K, V and P' = p * v_scale * 2^6 in FP16
  *   (round to nearest even); scores, softmax and sums are FP32. Results agree
  *   with sel_attn_prefill's to rounding, not bitwise; they depend on the order
  *   of each row's entries only through rounding, and identical inputs give

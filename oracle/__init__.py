@@ -7,7 +7,8 @@ The HIP path never calls it, links it or shares code with it.
 The arithmetic lives in sel_attn_oracle.c (plain C, FP64, OpenMP over query
 positions); this module builds it with gcc and marshals numpy arrays into it.
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
-(opt-in STRATA_PROMPT_ATTN_UNION=1)", sections Summary, Accuracy, Extra Notes.
+(opt-in STRATA_PROMPT_ATTN_UNION=1)", sections Summary (with its accuracy list)
+and Extra Notes.
 
 Every function here is pinned by tests/test_oracle_pins.py against dense
 brute force, closed forms and invariants; none is "parity unpinned".

@@ -9,14 +9,15 @@
  * XMX (opt-in STRATA_PROMPT_ATTN_UNION=1)".
  *
  * What is computed, as the page defines it:
- *   - Union (section Summary): for every 8 neighbouring query positions, the
- *     sorted union of their selected cells, each union cell marked with the
- *     positions that chose it. Section Extra Notes: a cell is an int32 and its
+ *   - Union (section Summary): one sorted list per group of 8 adjacent query
+ *     positions holding every cell any of them selected, each entry carrying
+ *     the set of group positions that selected it. Section Extra Notes: a cell is an int32 and its
  *     8-position mask a separate byte. Bit i of the mask is position 8g+i.
  *   - Attention (section Summary): every position attends to exactly the cells
  *     it selected, as the per-position FP32 kernel does; cells of pages that are
- *     not resident are masked (section Extra Notes, "Not tested" item; section
- *     Accuracy lists non-resident pages in the parity self-test). INT8 K/V are
+ *     not resident are masked (section Extra Notes, "Not tested" item; the
+ *     accuracy list in section Summary includes non-resident pages in the
+ *     parity self-test). INT8 K/V are
  *     dequantised with per-cell, per-KV-head scales. Query head h reads KV head
  *     h / q_per_kv. The softmax runs over the position's own set only.
  *
@@ -107,7 +108,7 @@ int oracle_union(int n_q, int sel_cap, int n_ctx, const int32_t* sel,
     int n_u = 0;
     for (int e = 0; e < n_all; ++e)
       if (n_u == 0 || all[n_u - 1] != all[e]) all[n_u++] = all[e];
-    /* mark each union cell with the positions that chose it */
+    /* the chooser byte of each union cell: one bit per group position that selected it */
     for (int u = 0; u < n_u; ++u) {
       uint8_t m = 0;
       for (int i = 0; i < n_pos; ++i)

@@ -7,8 +7,8 @@ shares no code with it.
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
 (opt-in STRATA_PROMPT_ATTN_UNION=1)". Section What changed lists the selection
 (block scores, then top-k) as the step that comes before the prompt attention,
-which the page leaves unchanged. Section Accuracy gives the selection layout's
-cap of 2,051 cells. The page does not say how blocks are scored, so the scores
+which the page leaves unchanged. The accuracy list in section Summary gives the
+selection layout's cap of 2,051 cells. The page does not say how blocks are scored, so the scores
 are an input here.
 
 Readings of what the page leaves open:

@@ -4,8 +4,8 @@
 // Page: #2808 "sycl: prompt attention over 8-query selection unions on XMX".
 // - Section Summary: the FP32 kernel in which every position gathers its own
 //   ~2,051 selected cells. That is the definition both paths compute.
-// - Section Extra Notes: the union kernel pays only when neighbouring
-//   selections overlap; with independent selections it is no faster. This
+// - Section Extra Notes: the union path wins only where adjacent positions'
+//   selections share cells and gains nothing when they are unrelated. This
 //   kernel serves that case: its gather is each position's own cells, not a
 //   union that can reach 8 times a selection.
 //

@@ -5,8 +5,9 @@
 //   section Summary: chunks of the union are dequantised once to FP16 (the
 //     page's chunks hold 64 cells, these 32);
 //     S^T = K Q^T and O += P V run on matrix units with FP32 sums for all 96 rows
-//     (8 positions x 12 heads); in the online softmax a cell is -inf for the
-//     positions that did not choose it; Q, K, V and P enter the products as FP16.
+//     (8 positions x 12 heads); a cell that a position did not select takes no
+//     part in that position's softmax (its logit counts as -inf); both products
+//     take their operands (Q, K, V, P) in FP16.
 //   section What changed: one work-group per 8 positions and KV head.
 //   section Extra Notes: cells of non-resident pages are masked.
 //
@@ -96,7 +97,7 @@ struct __align__(16) Smem {
   _Float16 k[kKStages][kChunk * kKRow]; // [cell][dim], rows of kKRow
   _Float16 v[kStages][kChunk * kD];     // [cell][dim], swizzled by v_pos()
   float kf[kStages][kChunk];            // k_scale * softmax_scale * log2(e); 0 where unusable
-  _Float16 vf[kStages][kChunk];         // FP16(v_scale * 2^9); 0 where unusable
+  _Float16 vf[kStages][kChunk];         // FP16(v_scale * 2^6); 0 where unusable
   uint32_t keep[kStages][4 * kChunk];   // keep masks, 16-byte units laid out by keep_unit()
   Ring ring[kRing];
 };

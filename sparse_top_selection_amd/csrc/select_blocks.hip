@@ -3,8 +3,8 @@
 //
 // Page: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
 // section What changed (the selection, block scores then top-k, is the step
-// before the prompt attention) and section Accuracy (the selection layout's cap
-// of 2,051 cells). A row is the three sink cells, the 31 earlier full blocks
+// before the prompt attention) and the accuracy list in section Summary (the
+// selection layout's cap of 2,051 cells). A row is the three sink cells, the 31 earlier full blocks
 // with the highest scores, and the position's own block up to the position:
 // 3 + 31*64 + 64 = 2,051 cells at most. A position with at most 31 earlier
 // blocks takes them all, so its row is [0, p]. Equal scores go to the lower

@@ -1,6 +1,6 @@
-// Union builder: for each group of 8 neighbouring query positions, the sorted
-// union of their selected cells and, per union cell, a byte whose bit i marks
-// position i of the group as one that chose it.
+// Union builder: for each group of 8 adjacent query positions, one sorted list
+// of every cell any of them selected and, per entry, a byte whose bit i is set
+// when position i of the group selected that cell.
 //
 // Page: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
 // section Summary (the union and its marks) and section What changed (one
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
   for (int round = 0; round < n_windows; ++round) {
     const int w0 = round * kWindowCells;
     const int win = min(kWindowCells, a.n_ctx - w0);
-    // the first batch's loads go out before the bitmap is cleared
+    // clear the window's bitmap (the barrier orders it before the marking)
     for (int i = tid; i < kWindowWords / 4; i += kThreads)
       reinterpret_cast<u32x4*>(bitmap)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();

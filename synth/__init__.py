@@ -8,7 +8,8 @@ the HIP path's tests and benchmark can use it.
 Page cited throughout: #2808 "sycl: prompt attention over 8-query selection
 unions on XMX (opt-in STRATA_PROMPT_ATTN_UNION=1)".
 
-Shapes the page fixes (section Accuracy, the parity self-test): random INT8
+Shapes the page fixes (the accuracy list in section Summary, the parity
+self-test): random INT8
 pools behind a shuffled page table, the prompt path's selection layout with a
 cap of 2,051 cells, contexts from 1.5K to 40K, ragged last groups, pages that
 are not resident. The page measures on a private model and private chats; these

@@ -5,8 +5,8 @@ import torch
 
 import sparse_top_selection_amd as sa
 
-# Tolerance on the attention output against the FP64 oracle. Q, K, V and the
-# probabilities enter the products as FP16, sums are FP32; the pages report
+# Tolerance on the attention output against the FP64 oracle. The products take
+# Q, K, V and the probabilities in FP16 and sum in FP32; the pages report
 # 2.6e-3 to 5.0e-3 max error against FP64 for such a kernel.
 MAX_ABS = 8e-3
 MEAN_ABS = 1e-3

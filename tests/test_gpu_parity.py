@@ -5,7 +5,7 @@ abs <= 1e-3 against FP64 on every workload, plus an exact-arithmetic case that
 catches a single wrong cell or mask bit, non-resident pages, empty rows, ragged
 groups, long contexts (several union windows) and a bitwise rerun.
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
-section Accuracy (the parity self-test's cases).
+the accuracy list in section Summary (the parity self-test's cases).
 """
 import dataclasses
 

@@ -3,9 +3,9 @@ the C ABI.
 
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX".
 Section Summary: every position gathers its own selected cells (the FP32
-kernel), which defines the output. Section Extra Notes: the union only pays
-when neighbouring selections overlap; this call serves batches where they do
-not. Gate as for the union path: max abs <= 8e-3 and mean abs <= 1e-3 against
+kernel), which defines the output. Section Extra Notes: the union path wins
+only where adjacent positions' selections share cells; this call serves
+batches where they do not. Gate as for the union path: max abs <= 8e-3 and mean abs <= 1e-3 against
 FP64, every output of every workload at full size.
 """
 import numpy as np

@@ -3,7 +3,8 @@ oracle, bit-exact on every row and length, through the C ABI.
 
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
 section What changed (the selection, block scores then top-k, precedes the
-prompt attention) and section Accuracy (the selection cap of 2,051).
+prompt attention) and the accuracy list in section Summary (the selection cap
+of 2,051).
 """
 import numpy as np
 import pytest

@@ -2,7 +2,8 @@
 
 Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
 section What changed (the selection, block scores then top-k, comes before the
-prompt attention) and section Accuracy (a selection holds at most 2,051 cells).
+prompt attention) and the accuracy list in section Summary (a selection holds
+at most 2,051 cells).
 The page prints no example, so the oracle is pinned by
 - a hand-worked fixture (ties, NaN, -0.0, sinks outside a dropped block 0,
   positions inside the first blocks);
