@@ -56,7 +56,7 @@ POS_CELL_BYTES = 128 + 128 + 4 + 4
 POS_ENTRY_BYTES = 4 + 4
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -82,7 +82,7 @@ def parse():
                     help="timing mode: share of far-block choices redrawn from one position to "
                          "the next (1.0 = independent selections)")
     ap.add_argument("--kv-heads", type=int, default=4, metavar="H", help="timing mode: KV heads")
-    ap.add_argument("--seed", type=int, default=2000, help="timing mode: input seed")
+    ap.add_argument("--seed", type=int, default=TIMING_SEED, help="timing mode: input seed")
     ap.add_argument("--kv-resident", type=float, default=1.0, metavar="F",
                     help="fraction of logical pages resident; the rest are marked -1 (seeded)")
     ap.add_argument("--cpu-rows", type=int, default=-1,
@@ -92,7 +92,7 @@ def parse():
     ap.add_argument("--summarize", metavar="DIR",
                     help="no GPU: turn the rocprofv3 output that profile.sh left in DIR into the "
                          "summaries under profiles/")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # the kernel sources behind each op's counters
@@ -305,6 +305,9 @@ def summarize(d: str, workload: str, op: str = "path"):
     print(json.dumps(rec, indent=1))
 
 
+TIMING_SEED = 2000   # the timing mode's default input seed
+
+
 def timing_workload(args):
     """The workload of the timing mode: the 32K chunk's recipe (INT8 pools with
     per-cell scales behind a shuffled page table, 3 sinks + own block + 31 far
@@ -315,9 +318,17 @@ def timing_workload(args):
     if not (0.0 <= args.drift <= 1.0):
         raise SystemExit("--drift must be in [0, 1]")
     name = "ctx%d_q%d_drift%g_kv%d" % (args.ctx, args.queries, args.drift, args.kv_heads)
+    if args.seed != TIMING_SEED:
+        name += "_seed%d" % args.seed
     return dataclasses.replace(synth.workload(synth.HEADLINE), name=name, n_ctx=args.ctx,
                                n_q=args.queries, n_kv=args.kv_heads, drift=args.drift,
                                seed=args.seed, n_pages=None)
+
+
+def measured_workload_name(args) -> str:
+    """The name of the workload a run with these arguments measures (the timing
+    mode's, else --workload's): profile summaries and counter records use it."""
+    return timing_workload(args).name if args.ctx else args.workload
 
 
 def main():
@@ -325,7 +336,7 @@ def main():
     if args.workload is None:
         args.workload = DEFAULT_WORKLOAD[args.op]
     if args.summarize:
-        summarize(args.summarize, args.workload, args.op)
+        summarize(args.summarize, measured_workload_name(args), args.op)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -435,8 +446,9 @@ def main():
         kv_bytes = union_cells * w.n_kv * UNION_KV_BYTES
         flops = union_cells * w.n_kv * 96 * FLOP_PER_CELL_ROW
     sec = prefill_ms * 1e-3
-    # the committed counters were taken on the workload's own inputs
-    custom = bool(args.sel or args.kv_resident < 1.0 or args.ctx)
+    # the committed counters were taken on the workload's own inputs (a timing-mode
+    # workload's name holds every argument that shapes its inputs)
+    custom = bool(args.sel or args.kv_resident < 1.0)
     rec = None if custom else counter_record(w.name, args.op)
     kernel = "prefill_positions_kernel" if positions else "sel_attn_prefill_kernel"
     traffic = None if rec is None else rec["kernels"][kernel]["hbm_bytes"]

@@ -52,3 +52,16 @@ def test_profile_summaries_name_their_commands():
         for c in cmds:
             assert "_work" not in c, c
             assert "$REPO/bench.py" in c, c
+
+
+def test_summaries_are_named_after_the_measured_workload():
+    args = bench.parse(["--summarize", "X", "--ctx", "32768", "--queries", "8192", "--drift", "0.76"])
+    args.workload = args.workload or bench.DEFAULT_WORKLOAD[args.op]
+    name = bench.measured_workload_name(args)
+    assert name == "ctx32768_q8192_drift0.76_kv4"
+    assert bench._profile_names(name, "path")[0] == "kernels_ctx32768_q8192_drift0.76_kv4_stats.txt"
+    args = bench.parse(["--summarize", "X", "--ctx", "32768", "--seed", "7"])
+    assert bench.measured_workload_name(args).endswith("_seed7")
+    args = bench.parse(["--summarize", "X"])
+    args.workload = bench.DEFAULT_WORKLOAD[args.op]
+    assert bench.measured_workload_name(args) == "ctx32k_drift005"
