@@ -621,18 +621,36 @@ struct Raw {
 // 4w..4w+3, w = 2q + hb, whose chooser bytes are word w of the ring's.
 __device__ __forceinline__ int keep_word(int ptid) { return 2 * ((ptid >> 3) & 3) + (ptid >> 5); }
 
-__device__ __forceinline__ void gather(const PrefillArgs& a, const Ring& rg, int ptid, Raw& r) {
+// What a gather reads from its ring slot, read one iteration ahead so that the
+// gather's loads need not wait for LDS.
+struct GatherAddr {
+  uint32_t off[4];
+  uint32_t soff;
+  uint32_t m;
+  uint32_t kw;
+};
+
+__device__ __forceinline__ GatherAddr gather_addr(const Ring& rg, int ptid) {
+  GatherAddr g;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) g.off[k] = task_offset(rg, ptid + 64 * k);
+  const int cell = ptid & (kChunk - 1);
+  g.soff = rg.off[cell];
+  g.m = rg.mask[cell];
+  g.kw = reinterpret_cast<const uint32_t*>(rg.mask)[keep_word(ptid)];
+  return g;
+}
+
+__device__ __forceinline__ void gather(const PrefillArgs& a, const GatherAddr& g, int ptid, Raw& r) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t off = task_offset(rg, ptid + 64 * k);
-    r.k[k] = *reinterpret_cast<const u32x4*>(a.k_pool + off);
-    r.v[k] = *reinterpret_cast<const u32x4*>(a.v_pool + off);
+    r.k[k] = *reinterpret_cast<const u32x4*>(a.k_pool + g.off[k]);
+    r.v[k] = *reinterpret_cast<const u32x4*>(a.v_pool + g.off[k]);
   }
-  const int cell = ptid & (kChunk - 1);
   const float* sp = (ptid < kChunk) ? a.k_scale : a.v_scale;
-  r.sc = sp[rg.off[cell] / kD];   // zeroed at conversion, when the load has landed
-  r.m = rg.mask[cell];
-  r.kw = reinterpret_cast<const uint32_t*>(rg.mask)[keep_word(ptid)];
+  r.sc = sp[g.soff / kD];   // zeroed at conversion, when the load has landed
+  r.m = g.m;
+  r.kw = g.kw;
 }
 
 // Keep masks from the chooser bytes of cells 4w..4w+3 (word w of the ring's
@@ -695,6 +713,7 @@ struct ProdState {
   Raw raw[4];
   UnionRec un[2];   // by pair parity
   PageRec pg[2];
+  GatherAddr ga;    // ring reads of the next iteration's gather
 };
 
 // Iteration c (phase P = c & 3), while the consumers work on chunks c-1..c+1.
@@ -721,8 +740,11 @@ __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, Pro
     ps.pg[s] = read_page_entry(a, ps.un[s]);
     ps.un[s] = read_union_entry(a, ubase, U, c + kPairUnion + hb, lane);
   }
-  gather(a, sm.ring[(c + kAheadGather) & (kRing - 1)], ptid, ps.raw[(P + kAheadGather) & 3]);
+  gather(a, ps.ga, ptid, ps.raw[(P + kAheadGather) & 3]);
   convert_k(stage(sm, P + 2), ptid, ps.raw[(P + 2) & 3]);
+  // the next gather's slot (chunk c+1+kAheadGather) is written by now: on even c
+  // just above, on odd c one iteration ago
+  ps.ga = gather_addr(sm.ring[(c + 1 + kAheadGather) & (kRing - 1)], ptid);
   lds_barrier();
 }
 
@@ -761,8 +783,9 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
       convert_k(stage(sm, 0), ptid, ps.raw[0]);
       convert_v(a, stage(sm, 0), ptid, lower, ps.raw[0], flags);
     }
-    gather(a, sm.ring[x], ptid, ps.raw[x & 3]);
+    gather(a, gather_addr(sm.ring[x], ptid), ptid, ps.raw[x & 3]);
   }
+  ps.ga = gather_addr(sm.ring[kAheadGather], ptid);
   // chunk 1's K tile (its V tile and factors open iteration 0)
   convert_k(stage(sm, 1), ptid, ps.raw[1]);
   lds_barrier();
