@@ -604,8 +604,10 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 // consumers work on chunks c and c+1): store chunk c+1's V tile and factors,
 // on even c translate a pair of chunks (union entries of c+14, c+15, page-table
 // entries of c+10, c+11, ring slots of c+6, c+7; lane half hb takes the pair's
-// chunk hb, cell ptid & 31), gather chunk c+kAheadGather into registers and
-// store the K tile of chunk c+2 (gathered kLead iterations earlier). Each
+// chunk hb, cell ptid & 31), gather chunk c+kAheadGather into registers (its
+// ring slot read at the end of the previous iteration), store the K tile of
+// chunk c+2 (gathered kLead iterations earlier) and read the ring slot of the
+// next iteration's gather. Each
 // thread owns tasks ptid + 64k (k = 0..3) of both pools, and the k scale
 // (ptid < 32) or v scale of cell ptid & 31.
 struct Raw {
