@@ -43,7 +43,8 @@ ROW_BYTES = 128 * 4 * 2        # q in + out, per (query position, query head)
 FLOP_PER_CELL_ROW = 4 * 128    # QK^T and PV, per (union cell, row)
 SELECT_RHO = 0.99              # AR(1) correlation of the block scores across positions
 # the kernel each op's roofline and counter summary is about
-OP_KERNELS = {"path": ("sel_attn_prefill_kernel", "union_build_kernel"),
+SPLIT_CALL = ("sel_attn_prefill_split_kernel", "prefill_merge_kernel")   # sel_attn_prefill_split's launches
+OP_KERNELS = {"path": ("sel_attn_prefill_kernel", "union_build_kernel") + SPLIT_CALL,
               "select": ("select_blocks_kernel",),
               "positions": ("prefill_positions_kernel",),
               "decode": ("decode_split_kernel", "decode_merge_kernel")}
@@ -96,7 +97,8 @@ def parse(argv=None):
 
 
 # the kernel sources behind each op's counters
-OP_SOURCES = {"path": ("union_build.hip", "sel_attn_prefill.hip"),
+OP_SOURCES = {"path": ("union_build.hip", "sel_attn_prefill.hip", "sel_attn_prefill_dev.h",
+                       "sel_attn_prefill_split.hip"),
               "select": ("select_blocks.hip",),
               "positions": ("prefill_positions.hip",),
               "decode": ("prefill_positions.hip",)}
@@ -152,14 +154,15 @@ def counter_traffic(workload_name: str, op: str = "path"):
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
-def measured_limiter(rec, kernel: str, alg_bytes: float):
-    """What the counters say bounds the kernel: HBM traffic against its
-    algorithmic bytes, and how busy the matrix cores were."""
-    if rec is None:
+def measured_limiter(rec, kernels, alg_bytes: float):
+    """What the counters say bounds the call's kernels (the first is the main
+    one): HBM traffic against their algorithmic bytes, and how busy the matrix
+    cores were."""
+    if rec is None or not all(k in rec["kernels"] for k in kernels):
         return None
-    traffic = rec["kernels"][kernel]["hbm_bytes"]
+    traffic = sum(rec["kernels"][k]["hbm_bytes"] for k in kernels)
     out = {"hbm_traffic_over_algorithmic_bytes": traffic / alg_bytes}
-    sq = rec.get("sq", {}).get(kernel)
+    sq = rec.get("sq", {}).get(kernels[0])
     if sq:
         d = sq["derived"]
         out["matrix_core_busy_frac"] = d.get("matrix-core busy / (4 x CU busy cycles)")
@@ -241,10 +244,10 @@ def summarize(d: str, workload: str, op: str = "path"):
     lines = ["rocprofv3 --kernel-trace --stats summary, workload %s%s" % (
                  workload, "" if op == "path" else ", op " + op),
              "command: " + commands[0], "",
-             "%-28s %6s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "total_%")]
+             "%-30s %6s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "total_%")]
     for r in stats:
-        lines.append("%-28s %6s %12.2f %12.2f %12.2f %12.2f" % (
-            _short(r["Name"])[:28], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+        lines.append("%-30s %6s %12.2f %12.2f %12.2f %12.2f" % (
+            _short(r["Name"])[:30], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", stats_name), "w") as f:
@@ -262,12 +265,16 @@ def summarize(d: str, workload: str, op: str = "path"):
         rec[counter] = {"copy_KiB": copy_kib, "factor": factor}
         for k in kernels:
             v = [float(r["Counter_Value"]) for r in rows if _short(r["Kernel_Name"]) == k]
+            if not v:   # not launched by this workload (the merge of a split prefill)
+                continue
             ent = rec["kernels"].setdefault(k, {})
             ent[counter + "_KiB_per_dispatch"] = float(np.mean(v))
             ent[counter.split("_")[0].lower() + "_bytes"] = float(np.mean(v)) * 1024.0 * factor
     for ent in rec["kernels"].values():
         ent["hbm_bytes"] = ent["fetch_bytes"] + ent["write_bytes"]
-    rec["hbm_bytes_per_launch"] = rec["kernels"][kernels[0]]["hbm_bytes"]
+    # the op's call: its first kernel, or for a split attention call its two launches
+    main = SPLIT_CALL if op == "path" and kernels[0] not in rec["kernels"] else kernels[:1]
+    rec["hbm_bytes_per_launch"] = sum(rec["kernels"][k]["hbm_bytes"] for k in main)
     with open(os.path.join(ROOT, "profiles", counters_name), "w") as f:
         json.dump(rec, f, indent=1)
     lines += ["", "HBM bytes per dispatch from counters (two --pmc runs, one counter each):"]
@@ -277,7 +284,7 @@ def summarize(d: str, workload: str, op: str = "path"):
                      COPY_BYTES >> 20, rec["FETCH_SIZE"]["copy_KiB"], rec["FETCH_SIZE"]["factor"],
                      rec["WRITE_SIZE"]["copy_KiB"], rec["WRITE_SIZE"]["factor"]))
     for k, ent in rec["kernels"].items():
-        lines.append("%-28s FETCH %.0f KiB -> %.1f MB, WRITE %.0f KiB -> %.1f MB, total %.1f MB" % (
+        lines.append("%-30s FETCH %.0f KiB -> %.1f MB, WRITE %.0f KiB -> %.1f MB, total %.1f MB" % (
             k, ent["FETCH_SIZE_KiB_per_dispatch"], ent["fetch_bytes"] / 1e6,
             ent["WRITE_SIZE_KiB_per_dispatch"], ent["write_bytes"] / 1e6, ent["hbm_bytes"] / 1e6))
     sq = _sq_summary(d, kernels)
@@ -395,6 +402,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     positions = args.op == "positions"
+    # grids too small to fill the GPU take the split call (workspace allocated here,
+    # outside the timed steps); the others the plain call, which is the same kernel
+    split_bytes = 0 if positions else sa.sel_attn_prefill_workspace_bytes(dims)
+    workspace = torch.empty(max(split_bytes, 16), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
@@ -408,6 +419,10 @@ def main():
             sa.sel_attn_prefill_positions(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"],
                                           t["v_scale"], t["page_table"], t["sel"], t["sel_len"],
                                           scale, out, status, stream)
+        elif split_bytes:
+            sa.sel_attn_prefill_split(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"],
+                                      t["v_scale"], t["page_table"], cells, mask, length, scale,
+                                      out, status, workspace, split_bytes, stream)
         else:
             sa.sel_attn_prefill(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"],
                                 t["v_scale"], t["page_table"], cells, mask, length, scale, out,
@@ -450,8 +465,13 @@ def main():
     # workload's name holds every argument that shapes its inputs)
     custom = bool(args.sel or args.kv_resident < 1.0)
     rec = None if custom else counter_record(w.name, args.op)
-    kernel = "prefill_positions_kernel" if positions else "sel_attn_prefill_kernel"
-    traffic = None if rec is None else rec["kernels"][kernel]["hbm_bytes"]
+    # the kernels of the timed attention call (a split call: its two launches)
+    call_kernels = (("prefill_positions_kernel",) if positions else
+                    SPLIT_CALL if split_bytes else ("sel_attn_prefill_kernel",))
+    kernel = " + ".join(call_kernels)
+    traffic = None
+    if rec is not None and all(k in rec["kernels"] for k in call_kernels):
+        traffic = sum(rec["kernels"][k]["hbm_bytes"] for k in call_kernels)
     kv_gbps = kv_bytes / sec / 1e9
     if positions:
         # The gathered rows (every listed cell of every position) are mostly
@@ -488,7 +508,7 @@ def main():
                 "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS},
             "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": F16_MFMA_PEAK_TFLOPS,
                      "frac": flops / sec / 1e12 / F16_MFMA_PEAK_TFLOPS},
-            "measured_limiter": measured_limiter(rec, kernel, kv_bytes),
+            "measured_limiter": measured_limiter(rec, call_kernels, kv_bytes),
         }
 
     if args.profile:
@@ -534,6 +554,9 @@ def main():
     if not positions:
         result["union"] = {"cells": union_cells, "mean_per_group": union_cells / g,
                            "ratio_to_mean_selection": (union_cells / g) / float(sel_len.mean())}
+        result["prefill_call"] = ("sel_attn_prefill_split (%d work-groups per (group, KV head), "
+                                  "then the merge)" % (split_bytes // (g * w.n_kv * 49920))
+                                  if split_bytes else "sel_attn_prefill")
 
     if args.cpu_rows != 0 and not args.profile:
         import oracle

@@ -199,6 +199,42 @@ int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_poo
                      float softmax_scale, float* out, uint32_t* status, hipStream_t stream);
 
 /*
+ * sel_attn_prefill_workspace_bytes - device workspace that sel_attn_prefill_split
+ * needs for these dims: groups x KV heads x splits x 49,920 bytes, with
+ * splits = min(16, ceil(512 / (groups x KV heads)), floor(C / 12)), where
+ * C = ceil(min(8 sel_cap, n_ctx) / 32) is the number of 32-cell chunks of the
+ * longest union the dims allow; 0 when splits <= 1 (groups x KV heads already
+ * give the GPU 512 work-groups, or the unions are too short to share out), and
+ * the call then runs exactly as sel_attn_prefill.
+ */
+size_t sel_attn_prefill_workspace_bytes(const sel_attn_dims* d);
+
+/*
+ * sel_attn_prefill_split - sel_attn_prefill for grids too small to fill the GPU
+ * (the same attention over the same unions, section Summary). Each group's
+ * union is divided at 32-cell chunk boundaries over `splits` work-groups, each
+ * of which runs the same online softmax over its share and writes its
+ * unnormalised state (running maximum, probability sum, O) to the workspace; a
+ * second kernel merges the shares of every row (weights exp2(m_s - max m)) and
+ * writes out. Results agree with sel_attn_prefill's to rounding, not bitwise
+ * (the sums are grouped differently); they are deterministic.
+ *
+ *   arguments    as for sel_attn_prefill, plus:
+ *   workspace    device memory of at least workspace_bytes =
+ *                sel_attn_prefill_workspace_bytes(d), 16-byte aligned, owned by
+ *                the caller; may be NULL when that size is 0. Calls that run
+ *                at the same time need workspaces of their own.
+ *   Errors: as sel_attn_prefill; a workspace that is NULL, too small or
+ *   misaligned while one is needed gives EINVAL.
+ */
+int sel_attn_prefill_split(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                           const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                           const int32_t* page_table, const int32_t* union_cells,
+                           const uint8_t* union_mask, const int32_t* union_len,
+                           float softmax_scale, float* out, uint32_t* status, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * sel_attn_prefill_positions - the same attention as sel_attn_build_union +
  * sel_attn_prefill, computed per position with no union: every position
  * gathers its own selected cells (section Summary: the FP32 kernel in which

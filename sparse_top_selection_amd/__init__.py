@@ -7,8 +7,9 @@ fallback: importing this package fails loudly when libselattn.so is missing,
 and every call raises when the library returns an error code.
 
 The functions named like the C entry points (sel_attn_select_blocks,
-sel_attn_build_union, sel_attn_prefill, sel_attn_prefill_positions,
-sel_attn_decode, sel_attn_decode_workspace_bytes, sel_attn_last_error) take
+sel_attn_build_union, sel_attn_prefill, sel_attn_prefill_workspace_bytes,
+sel_attn_prefill_split, sel_attn_prefill_positions, sel_attn_decode,
+sel_attn_decode_workspace_bytes, sel_attn_decode_noalloc, sel_attn_last_error) take
 preallocated device tensors and mirror include/sel_attn.h one to one.
 select_blocks(), build_union(), prefill(), prefill_positions(), decode() and
 check_status() are conveniences that allocate outputs and read the status word.
@@ -57,6 +58,7 @@ DECODE_MAX_Q = 65535
 DECODE_NOALLOC_MAX_BYTES = 8388608
 
 EXPORTED = ("sel_attn_select_blocks", "sel_attn_build_union", "sel_attn_prefill",
+            "sel_attn_prefill_workspace_bytes", "sel_attn_prefill_split",
             "sel_attn_prefill_positions", "sel_attn_decode_workspace_bytes", "sel_attn_decode",
             "sel_attn_decode_noalloc", "sel_attn_last_error")
 
@@ -82,6 +84,11 @@ _lib.sel_attn_build_union.restype = ctypes.c_int
 _lib.sel_attn_prefill.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                   ctypes.c_float, _p, _p, _p]
 _lib.sel_attn_prefill.restype = ctypes.c_int
+_lib.sel_attn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+_lib.sel_attn_prefill_workspace_bytes.restype = ctypes.c_size_t
+_lib.sel_attn_prefill_split.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                        ctypes.c_float, _p, _p, _p, ctypes.c_size_t, _p]
+_lib.sel_attn_prefill_split.restype = ctypes.c_int
 _lib.sel_attn_prefill_positions.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
                                             ctypes.c_float, _p, _p, _p]
 _lib.sel_attn_prefill_positions.restype = ctypes.c_int
@@ -152,6 +159,24 @@ def sel_attn_prefill(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table
                                  _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
                                  ctypes.c_float(float(softmax_scale)), _ptr(out), _ptr(status),
                                  _stream(stream)))
+
+
+def sel_attn_prefill_workspace_bytes(dims: Dims) -> int:
+    """Workspace bytes sel_attn_prefill_split needs for these dims (0: it does not split)."""
+    return int(_lib.sel_attn_prefill_workspace_bytes(ctypes.byref(dims)))
+
+
+def sel_attn_prefill_split(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table,
+                           union_cells, union_mask, union_len, softmax_scale: float, out, status,
+                           workspace, workspace_bytes: int, stream=None) -> None:
+    """Enqueue the attention step, splitting small grids over the workspace (see
+    include/sel_attn.h). Tensors or raw device pointers."""
+    _check(_lib.sel_attn_prefill_split(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(k_scale), _ptr(v_scale), _ptr(page_table),
+                                       _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
+                                       ctypes.c_float(float(softmax_scale)), _ptr(out),
+                                       _ptr(status), _ptr(workspace), ctypes.c_size_t(workspace_bytes),
+                                       _stream(stream)))
 
 
 def sel_attn_prefill_positions(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table, sel,
@@ -303,8 +328,11 @@ def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, status=Non
 
 
 def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_mask, union_len,
-            softmax_scale: float, n_ctx: int, status=None, stream=None, out=None):
-    """Attention over each group's union. Returns (out, status)."""
+            softmax_scale: float, n_ctx: int, status=None, stream=None, out=None, split=False,
+            workspace=None):
+    """Attention over each group's union. With split=True, grids too small for
+    the GPU are split over a workspace (uint8 device tensor, allocated when not
+    given; see sel_attn_prefill_split). Returns (out, status)."""
     dev = _on_gpu(q, "q")
     _need(q, "q", torch.float32, 3, dev)
     for name, t, dt, nd in (("k_pool", k_pool, torch.int8, 4), ("v_pool", v_pool, torch.int8, 4),
@@ -335,8 +363,18 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
         _need_shape(out, "out", torch.float32, q.shape, dev)
     status = _status_for(status, dev)
     dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=cap, head_dim=hd, page_size=ps)
-    sel_attn_prefill(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
-                     union_mask, union_len, softmax_scale, out, status, stream)
+    if not split:
+        sel_attn_prefill(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
+                         union_mask, union_len, softmax_scale, out, status, stream)
+        return out, status
+    need = sel_attn_prefill_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    sel_attn_prefill_split(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
+                           union_mask, union_len, softmax_scale, out, status, workspace,
+                           workspace.numel() * workspace.element_size(), stream)
     return out, status
 
 

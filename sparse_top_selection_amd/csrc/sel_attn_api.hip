@@ -14,6 +14,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "sel_attn_internal.h"
@@ -161,21 +162,31 @@ int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32
   return SEL_ATTN_OK;
 }
 
-int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
-                     const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                     const int32_t* page_table, const int32_t* union_cells,
-                     const uint8_t* union_mask, const int32_t* union_len, float softmax_scale,
-                     float* out, uint32_t* status, hipStream_t stream) {
-  static const char* who = "sel_attn_prefill";
+}  // extern "C"
+
+namespace {
+
+int64_t prefill_items(const sel_attn_dims* d) { return (int64_t)((d->n_q + 7) / 8) * d->n_kv; }
+
+// the most cells a group's union can hold: 8 rows of sel_cap, within the context
+int64_t prefill_max_cells(const sel_attn_dims* d) {
+  return std::min<int64_t>(8LL * d->sel_cap, (int64_t)d->n_ctx);
+}
+
+// Checks shared by sel_attn_prefill and sel_attn_prefill_split, and the kernel
+// arguments (one work-group per (group, KV head) and split).
+int prefill_args(const sel_attn_dims* d, const char* who, const float* q, const int8_t* k_pool,
+                 const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                 const int32_t* page_table, const int32_t* union_cells, const uint8_t* union_mask,
+                 const int32_t* union_len, float softmax_scale, float* out, uint32_t* status,
+                 selattn::PrefillArgs& a, void* workspace = nullptr, size_t workspace_bytes = 0,
+                 bool split = false) {
   int rc = check_dims(d, who);
   if (rc) return rc;
   if (!status) return fail(SEL_ATTN_EINVAL, "%s: status is NULL", who);
   if (!isfinite(softmax_scale))
     return fail(SEL_ATTN_EINVAL, "%s: softmax_scale must be finite", who);
-  if (d->n_q == 0) {
-    g_err[0] = 0;
-    return SEL_ATTN_OK;
-  }
+  if (d->n_q == 0) return 0;
   if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !union_cells ||
       !union_mask || !union_len || !out)
     return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
@@ -184,9 +195,18 @@ int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_poo
   if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(page_table, 4) ||
       !aligned(union_cells, 4) || !aligned(union_len, 4) || !aligned(status, 4))
     return fail(SEL_ATTN_EINVAL, "%s: scale and int32 arrays must be 4-byte aligned", who);
+  const int64_t items = (int64_t)((d->n_q + 7) / 8) * d->n_kv;
+  const int splits = split ? selattn::prefill_split_count(items, prefill_max_cells(d)) : 1;
+  if (splits > 1) {
+    const size_t need = (size_t)items * splits * sizeof(selattn::PrefillPartial);
+    if (!workspace || workspace_bytes < need)
+      return fail(SEL_ATTN_EINVAL, "%s: workspace of %zu bytes, %zu needed", who,
+                  workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned(workspace, 16))
+      return fail(SEL_ATTN_EINVAL, "%s: workspace must be 16-byte aligned", who);
+  }
   rc = check_device(who);
   if (rc) return rc;
-  selattn::PrefillArgs a;
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -205,9 +225,62 @@ int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_poo
   a.n_pages = d->n_pages;
   a.sel_cap = d->sel_cap;
   a.n_groups = (d->n_q + 7) / 8;
-  const int64_t n_wg = (int64_t)a.n_groups * d->n_kv;
-  a.per_xcd = (int32_t)((n_wg + 7) / 8);
+  a.n_splits = splits;
+  a.part = splits > 1 ? static_cast<selattn::PrefillPartial*>(workspace) : nullptr;
+  a.per_xcd = (int32_t)((items * splits + 7) / 8);
+  return 0;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                     const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                     const int32_t* page_table, const int32_t* union_cells,
+                     const uint8_t* union_mask, const int32_t* union_len, float softmax_scale,
+                     float* out, uint32_t* status, hipStream_t stream) {
+  static const char* who = "sel_attn_prefill";
+  selattn::PrefillArgs a;
+  int rc = prefill_args(d, who, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
+                        union_mask, union_len, softmax_scale, out, status, a);
+  if (rc) return rc;
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
   hipError_t e = selattn::launch_prefill(a, stream);
+  if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
+  g_err[0] = 0;
+  return SEL_ATTN_OK;
+}
+
+size_t sel_attn_prefill_workspace_bytes(const sel_attn_dims* d) {
+  if (!d || d->n_q <= 0 || d->n_kv <= 0) return 0;
+  const int64_t items = prefill_items(d);
+  const int splits = selattn::prefill_split_count(items, prefill_max_cells(d));
+  return splits > 1 ? (size_t)items * splits * sizeof(selattn::PrefillPartial) : 0;
+}
+
+int sel_attn_prefill_split(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
+                           const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                           const int32_t* page_table, const int32_t* union_cells,
+                           const uint8_t* union_mask, const int32_t* union_len,
+                           float softmax_scale, float* out, uint32_t* status, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  static const char* who = "sel_attn_prefill_split";
+  selattn::PrefillArgs a;
+  int rc = prefill_args(d, who, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
+                        union_mask, union_len, softmax_scale, out, status, a, workspace,
+                        workspace_bytes, true);
+  if (rc) return rc;
+  if (d->n_q == 0) {
+    g_err[0] = 0;
+    return SEL_ATTN_OK;
+  }
+  hipError_t e = a.n_splits > 1 ? selattn::launch_prefill_split(a, stream)
+                                 : selattn::launch_prefill(a, stream);
   if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
   g_err[0] = 0;
   return SEL_ATTN_OK;

@@ -40,7 +40,39 @@ struct PrefillArgs {
   int32_t sel_cap;
   int32_t n_groups;
   int32_t per_xcd;     // workgroups each XCD walks through (grid = 8 * per_xcd)
+  int32_t n_splits;    // work-groups per (group, KV head): 1 writes out directly,
+                       // more write PrefillPartial records that a merge combines
+  struct PrefillPartial* part;   // [n_groups * n_kv][n_splits] when n_splits > 1
 };
+
+// One split of a (group, KV head)'s union: for each of the 96 rows, the running
+// maximum (log2 domain), the probability sum and O (2^6 times sum p v, the V
+// offset removed), unnormalised.
+struct PrefillPartial {
+  float m[96];
+  float l[96];
+  float o[96][128];
+};
+
+// Work-groups per (group, KV head) that sel_attn_prefill_split uses for a grid
+// of n_items = groups * KV heads whose unions hold at most max_cells cells
+// (min(8 sel_cap, n_ctx)): enough to give the GPU kPrefillSplitTarget
+// work-groups when the grid alone is smaller, at most 16, and no more than
+// leave each split kPrefillMinSplitChunks chunks of the longest possible union.
+// A split work-group's fixed cost (three dependent memory round trips before
+// its first chunk, its record written and flushed, its share of the merge) is
+// about the time of 8 to 12 chunks, so shorter shares gain nothing.
+constexpr int kPrefillSplitTarget = 512;
+constexpr int kPrefillMaxSplits = 16;
+constexpr int kPrefillMinSplitChunks = 12;
+inline int prefill_split_count(int64_t n_items, int64_t max_cells) {
+  if (n_items <= 0 || n_items >= kPrefillSplitTarget) return 1;
+  int64_t s = (kPrefillSplitTarget + n_items - 1) / n_items;
+  if (s > kPrefillMaxSplits) s = kPrefillMaxSplits;
+  const int64_t by_len = ((max_cells > 0 ? max_cells : 0) + 31) / 32 / kPrefillMinSplitChunks;
+  if (s > by_len) s = by_len;
+  return s > 1 ? (int)s : 1;
+}
 
 struct SelectArgs {
   const float* scores;   // [n_q][n_blocks]
@@ -88,5 +120,6 @@ hipError_t launch_prefill_positions(const PositionsArgs& a, hipStream_t stream);
 hipError_t launch_decode(const PositionsArgs& a, DecodePartial* part, hipStream_t stream);
 hipError_t launch_union_build(const UnionArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_split(const PrefillArgs& a, hipStream_t stream);   // n_splits > 1
 
 }  // namespace selattn

@@ -22,6 +22,8 @@ def test_header_declares_the_entry_points():
                                     "sel_attn_decode_noalloc",
                                     "sel_attn_decode_workspace_bytes", "sel_attn_last_error",
                                     "sel_attn_prefill", "sel_attn_prefill_positions",
+                                    "sel_attn_prefill_split",
+                                    "sel_attn_prefill_workspace_bytes",
                                     "sel_attn_select_blocks"]
 
 
@@ -312,3 +314,32 @@ def test_status_word_is_the_headers_uint32():
     st = sa.new_status(torch.device("cpu"))
     assert st.dtype == torch.uint32 and tuple(st.shape) == (1,) and sa.status_value(st) == 0
     assert sa.check_status(st) == 0
+
+
+def test_prefill_split_workspace_size_and_host_errors():
+    """sel_attn_prefill_split needs a workspace only when the grid is small, of
+    groups x KV heads x splits records of 49,920 bytes; a missing or short one
+    is refused before the device is touched."""
+    import sparse_top_selection_amd as sa
+    big = _dims(n_ctx=32768, n_q=8192, n_kv=4)
+    assert sa.sel_attn_prefill_workspace_bytes(big) == 0      # 4,096 work-groups: no split
+    long = _dims(n_ctx=65536, n_q=32, n_kv=4)                 # 16 items: 16 splits each
+    assert sa.sel_attn_prefill_workspace_bytes(long) == 16 * 16 * 49920
+    mid = _dims(n_ctx=8192, n_q=1024, n_kv=1)                 # 128 items: 4 splits each
+    assert sa.sel_attn_prefill_workspace_bytes(mid) == 128 * 4 * 49920
+    small = _dims(n_ctx=1536, n_q=250, n_kv=1)                # 32 items, at most 48 chunks: 4 splits
+    assert sa.sel_attn_prefill_workspace_bytes(small) == 32 * 4 * 49920
+    capped = _dims(n_ctx=65536, n_q=16, n_kv=1, sel_cap=40)   # unions of at most 320 cells: 10 chunks
+    assert sa.sel_attn_prefill_workspace_bytes(capped) == 0
+    assert sa.sel_attn_prefill_workspace_bytes(_dims(n_ctx=300, n_q=16, n_kv=1)) == 0
+    assert sa.sel_attn_prefill_workspace_bytes(_dims(n_q=0)) == 0
+    args = (FAKE,) * 9
+    for ws, nbytes in ((None, 0), (FAKE, 32 * 4 * 49920 - 1)):
+        with pytest.raises(sa.SelAttnError) as e:
+            sa.sel_attn_prefill_split(small, *args, 0.1, FAKE, FAKE, ws, nbytes, stream=0)
+        assert e.value.code == -1 and "workspace" in sa.sel_attn_last_error()
+    with pytest.raises(sa.SelAttnError) as e:
+        sa.sel_attn_prefill_split(small, *args, 0.1, FAKE, FAKE, FAKE + 8, 32 * 4 * 49920, stream=0)
+    assert e.value.code == -1 and "aligned" in sa.sel_attn_last_error()
+    sa.sel_attn_prefill_split(_dims(n_q=0), *(None,) * 9, 0.1, None, FAKE, None, 0, stream=0)
+    assert sa.sel_attn_last_error() == ""
