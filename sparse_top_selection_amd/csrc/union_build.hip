@@ -14,7 +14,9 @@
 //     int32. It is read with 16-byte loads of the aligned 16-byte blocks that
 //     overlap it (a block holding one byte of the span lies in a mapped page),
 //     in batches of four per thread whose loads are all issued before the first
-//     is used; entries outside the span or past their row's length are skipped.
+//     is used (the first batch at entry, before the row lengths are read and
+//     the bitmap cleared); entries outside the span or past their row's length
+//     are skipped.
 //   * Every counted entry ORs bit i (its row) into the chooser byte of its cell
 //     in an LDS bitmap of one byte per cell, 32K cells per window (ds_or
 //     atomics); longer contexts take several windows in ascending order, each
@@ -113,6 +115,12 @@ __device__ __forceinline__ void scatter_block(uint32_t* bitmap, const i32x4 x, u
   }
 }
 
+// zero the window's chooser bytes
+__device__ __forceinline__ void clear_bitmap(uint32_t* bitmap, int tid) {
+  for (int i = tid; i < kWindowWords / 4; i += kThreads)
+    reinterpret_cast<u32x4*>(bitmap)[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
@@ -134,6 +142,23 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
   int32_t* out_cells = a.union_cells + (int64_t)g * ucap;
   uint8_t* out_mask = a.union_mask + (int64_t)g * ucap;
 
+  // the span: n_pos rows from sel + 8g * cap, read as the aligned 16-byte
+  // blocks that overlap it; flat index f of a loaded entry = 4 * block - shift
+  const int32_t* span = a.sel + (int64_t)8 * g * cap;
+  const int shift = (int)((reinterpret_cast<uintptr_t>(span) >> 2) & 3u);
+  const int32_t* base = span - shift;
+  const int span_len = n_pos * cap;
+  const float inv_cap = 1.f / (float)cap;
+
+  // blocks of the span's aligned 16-byte cover
+  const int n_blocks = (int)(((int64_t)span_len + shift + 3) / 4);
+
+  // the first batch of blocks goes out before anything waits: it needs neither
+  // the row lengths (read next) nor the cleared bitmap until it is scattered
+  i32x4 first[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) first[k] = load_block(base, tid + kThreads * k, n_blocks);
+
   uint32_t flags = 0;
   if (tid < 8) {
     int L = 0;
@@ -146,34 +171,39 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
     }
     row_end[tid] = tid * cap + L;
   }
-
-  // the span: n_pos rows from sel + 8g * cap, read as the aligned 16-byte
-  // blocks that overlap it; flat index f of a loaded entry = 4 * block - shift
-  const int32_t* span = a.sel + (int64_t)8 * g * cap;
-  const int shift = (int)((reinterpret_cast<uintptr_t>(span) >> 2) & 3u);
-  const int32_t* base = span - shift;
-  const int span_len = n_pos * cap;
-  const float inv_cap = 1.f / (float)cap;
-
-  // blocks of the span's aligned 16-byte cover
-  const int n_blocks = (int)(((int64_t)span_len + shift + 3) / 4);
   __syncthreads();   // row_end
 
   int written = 0;  // union cells emitted so far (same value in every thread)
   // windows counted, not stepped, so that no cell index passes INT32_MAX
   const int n_windows = (int)(((int64_t)a.n_ctx + kWindowCells - 1) / kWindowCells);
+
+  // the first window's bitmap cleared (the barrier orders it before the
+  // marking) and its first batch scattered, here rather than in the loop so
+  // that the batch's registers are free before it
+  clear_bitmap(bitmap, tid);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int b = tid + kThreads * k;
+    if (b < n_blocks)
+      scatter_block(bitmap, first[k],
+                    classify_block(first[k], 4 * b - shift, cap, inv_cap, row_end, a.n_ctx, flags), 0,
+                    min(kWindowCells, a.n_ctx));
+  }
+
   for (int round = 0; round < n_windows; ++round) {
     const int w0 = round * kWindowCells;
     const int win = min(kWindowCells, a.n_ctx - w0);
-    // clear the window's bitmap (the barrier orders it before the marking)
-    for (int i = tid; i < kWindowWords / 4; i += kThreads)
-      reinterpret_cast<u32x4*>(bitmap)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
+    if (round > 0) {
+      clear_bitmap(bitmap, tid);
+      __syncthreads();
+    }
 
     // scatter: the span in batches of kBatch blocks per thread, all loads of a
     // batch issued before the first is used (one memory round trip per batch;
-    // later windows find the span in cache)
-    for (int b0 = 0; b0 < n_blocks; b0 += kThreads * kBatch) {
+    // the first window's first batch is done above, later windows find the
+    // span in cache)
+    for (int b0 = round == 0 ? kThreads * kBatch : 0; b0 < n_blocks; b0 += kThreads * kBatch) {
       i32x4 raw[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) raw[k] = load_block(base, b0 + tid + kThreads * k, n_blocks);
