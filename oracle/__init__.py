@@ -11,7 +11,9 @@ Page cited: #2808 "sycl: prompt attention over 8-query selection unions on XMX
 and Extra Notes.
 
 Every function here is pinned by tests/test_oracle_pins.py against dense
-brute force, closed forms and invariants; none is "parity unpinned".
+brute force, closed forms, invariants and hand-worked fixtures; none is
+"parity unpinned". union_rows is plain numpy: a definition, not arithmetic
+worth a C loop.
 
 The selection step before the path (block scores -> selection rows) lives in
 oracle/selection.py (numpy), pinned by tests/test_selection_oracle.py.
@@ -92,6 +94,38 @@ def union(sel: np.ndarray, sel_len: np.ndarray, n_ctx: int):
     if rc != 0:
         raise ValueError("oracle_union: invalid selection (rc=%d)" % rc)
     return cells, mask, length
+
+
+PAGE_RANGE = 4   # the status bit union_rows reports for a page-table entry outside [-1, n_pages)
+
+
+def union_rows(cells: np.ndarray, length: np.ndarray, page_table: np.ndarray, n_kv: int,
+               n_pages: int, page_size: int = 64):
+    """The pool row, for KV head 0, of every union cell.
+
+    Pools are [n_pages][n_kv][page_size][head_dim] and scales
+    [n_pages][n_kv][page_size], so flattened to rows, cell c of physical page
+    p = page_table[c // page_size] sits at row (p * n_kv + h) * page_size +
+    c % page_size for KV head h: the KV-head-0 row plus h * page_size. A page
+    that is not resident (-1) gives -1 (its cells are masked for every
+    position: page section Extra Notes); an entry outside [-1, n_pages) gives
+    -1 and sets the PAGE_RANGE flag. Entries past length[g] are 0.
+    Returns (rows int32 like cells, flags).
+    """
+    cells = np.asarray(cells, np.int64)
+    length = np.asarray(length, np.int64)
+    page_table = np.asarray(page_table, np.int64)
+    rows = np.zeros(cells.shape, np.int32)
+    flags = 0
+    for g in range(cells.shape[0]):
+        c = cells[g, :length[g]]
+        p = page_table[c // page_size]
+        bad = (p < -1) | (p >= n_pages)
+        if bad.any():
+            flags |= PAGE_RANGE
+        ok = (p >= 0) & (p < n_pages)
+        rows[g, :length[g]] = np.where(ok, p * n_kv * page_size + c % page_size, -1)
+    return rows, flags
 
 
 def attention(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,

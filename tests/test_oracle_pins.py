@@ -351,3 +351,48 @@ def test_union_empty_rows():
     cells, mask, length = oracle.union(sel, sel_len, 10)
     assert length.tolist() == [2]
     assert cells[0, :2].tolist() == [1, 7] and mask[0, :2].tolist() == [32, 32]
+
+
+# --------------------------------------------------------------------------
+# union rows (each union cell resolved through the page table once)
+# --------------------------------------------------------------------------
+def test_union_rows_golden_fixture():
+    lines = [l.strip() for l in open(os.path.join(GOLDEN, "union_rows_example.txt"))
+             if l.strip() and not l.startswith("#")]
+    field = {l.split(":")[0]: list(map(int, l.split(":")[1].split())) for l in lines}
+    cells = np.array([field["cells"]], np.int32)
+    length = np.array([len(field["cells"])], np.int32)
+    rows, flags = oracle.union_rows(cells, length, np.array(field["page_table"], np.int32),
+                                    n_kv=2, n_pages=8)
+    assert rows[0].tolist() == field["rows"]
+    assert flags == field["flags"][0]
+
+
+@pytest.mark.parametrize("seed,n_kv,nonres", [(0, 1, 0.0), (1, 3, 0.3), (2, 4, 0.6)])
+def test_union_rows_address_the_cells_pool_entries(seed, n_kv, nonres):
+    """Flattened to rows, each pool and scale array holds cell c of KV head h at
+    union row + 64 h: the same bytes as indexing the pool by (page, head, slot);
+    rows of non-resident pages are -1, and only they."""
+    d = synth.small_random(seed, n_ctx=3000, n_q=21, n_kv=n_kv, dup_frac=0.2,
+                           nonresident_frac=nonres, pool_extra=2)
+    cells, mask, length = oracle.union(d["sel"], d["sel_len"], d["n_ctx"])
+    n_pages = d["k_pool"].shape[0]
+    rows, flags = oracle.union_rows(cells, length, d["page_table"], n_kv, n_pages)
+    assert flags == 0
+    flat = {k: d[k].reshape(n_pages * n_kv * 64, -1) for k in ("k_pool", "v_pool")}
+    flat_s = {k: d[k].reshape(-1) for k in ("k_scale", "v_scale")}
+    checked = 0
+    for g in range(length.size):
+        for c, r in zip(cells[g, :length[g]].tolist(), rows[g, :length[g]].tolist()):
+            page = int(d["page_table"][c // 64])
+            assert (r == -1) == (page == -1)
+            if page < 0:
+                continue
+            for h in range(n_kv):
+                for k in ("k_pool", "v_pool"):
+                    assert np.array_equal(flat[k][r + 64 * h], d[k][page, h, c % 64])
+                for k in ("k_scale", "v_scale"):
+                    assert flat_s[k][r + 64 * h] == d[k][page, h, c % 64]
+                checked += 1
+    assert checked > 100
+    assert nonres == 0.0 or (rows[rows != 0] == -1).any()
