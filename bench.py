@@ -35,9 +35,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix
 # algorithmic bytes per union cell per (group, KV head) workgroup:
 #   K row 128 + V row 128 + k_scale 4 + v_scale 4 (the union K/V bytes: 264)
-#   + union cell index 4 + chooser byte 1 + page-table entry 4
+#   + union pool row 4 + chooser byte 1
 UNION_KV_BYTES = 264
-UNION_CELL_BYTES = UNION_KV_BYTES + 4 + 1   # + union cell index and chooser byte
+UNION_CELL_BYTES = UNION_KV_BYTES + 4 + 1   # + union pool row and chooser byte
 RIDGE_FLOP_PER_BYTE = F16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROW_BYTES = 128 * 4 * 2        # q in + out, per (query position, query head)
 FLOP_PER_CELL_ROW = 4 * 128    # QK^T and PV, per (union cell, row)
@@ -394,6 +394,7 @@ def main():
     cap = w.sel_cap
     cells = torch.empty((g, 8 * cap), dtype=torch.int32, device=dev)
     mask = torch.empty((g, 8 * cap), dtype=torch.uint8, device=dev)
+    rows = torch.empty((g, 8 * cap), dtype=torch.int32, device=dev)
     length = torch.empty(g, dtype=torch.int32, device=dev)
     out = torch.empty_like(t["q"])
     status = sa.new_status(dev)
@@ -411,8 +412,8 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         if not positions:
-            sa.sel_attn_build_union(dims, t["sel"], t["sel_len"], cells, mask, length, status,
-                                    stream)
+            sa.sel_attn_build_union(dims, t["sel"], t["sel_len"], t["page_table"], cells, mask,
+                                    rows, length, status, stream)
         if ev is not None:
             ev[1].record(stream)
         if positions:
@@ -421,12 +422,11 @@ def main():
                                           scale, out, status, stream)
         elif split_bytes:
             sa.sel_attn_prefill_split(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"],
-                                      t["v_scale"], t["page_table"], cells, mask, length, scale,
-                                      out, status, workspace, split_bytes, stream)
+                                      t["v_scale"], rows, mask, length, scale, out, status,
+                                      workspace, split_bytes, stream)
         else:
             sa.sel_attn_prefill(dims, t["q"], t["k_pool"], t["v_pool"], t["k_scale"],
-                                t["v_scale"], t["page_table"], cells, mask, length, scale, out,
-                                status, stream)
+                                t["v_scale"], rows, mask, length, scale, out, status, stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -502,7 +502,7 @@ def main():
             "intensity_flop_per_byte": intensity,
             "ridge_flop_per_byte": RIDGE_FLOP_PER_BYTE,
             "with_indices_and_q_out": {
-                "basis": "+ 5 B of union index and chooser byte per union cell and KV head, "
+                "basis": "+ 5 B of union pool row and chooser byte per union cell and KV head, "
                          "+ 98,304 B of q in and out per work-group",
                 "bytes_per_launch": alg_bytes, "achieved": alg_bytes / sec / 1e9,
                 "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS},

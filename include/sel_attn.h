@@ -64,9 +64,10 @@ extern "C" {
 #define SEL_ATTN_ELAUNCH (-3)      /* a HIP call failed (device query or kernel launch) */
 
 /* Bits the kernels OR into *status. */
-#define SEL_ATTN_STATUS_CELL_RANGE 1u  /* a selected or union cell outside [0, n_ctx) */
+#define SEL_ATTN_STATUS_CELL_RANGE 1u  /* a selected cell outside [0, n_ctx) */
 #define SEL_ATTN_STATUS_SEL_LEN 2u     /* sel_len[j] outside [0, sel_cap] */
-#define SEL_ATTN_STATUS_PAGE_RANGE 4u  /* page_table entry >= n_pages (or < -1) */
+#define SEL_ATTN_STATUS_PAGE_RANGE 4u  /* page_table entry >= n_pages (or < -1), or a union
+                                          row past the pools */
 #define SEL_ATTN_STATUS_UNION_LEN 8u   /* union_len[g] outside [0, 8*sel_cap] */
 #define SEL_ATTN_STATUS_V_SCALE 16u    /* a v_scale of a used cell with |v_scale| >= 4 or not finite */
 
@@ -132,34 +133,49 @@ int sel_attn_select_blocks(const sel_attn_dims* d, int32_t first_pos, const floa
  * sel_attn_build_union - the union step (section Summary: per group of 8
  * adjacent positions, one sorted list of every cell any of them selected, each
  * entry tagged with which of the 8 selected it; section What changed: one
- * work-group per 8 positions with local bitmaps).
+ * work-group per 8 positions with local bitmaps; section Extra Notes: cells of
+ * pages that are not resident are masked). Each union cell is also resolved
+ * through the page table here, once, rather than by every KV head's work-group
+ * of sel_attn_prefill.
  *
  *   sel          const int32 [n_q][sel_cap]   selected logical cells of each
  *                                             query index; any order, repeats
  *                                             allowed (a cell counts once)
  *   sel_len      const int32 [n_q]            valid entries of each row
+ *   page_table   const int32 [ceil(n_ctx/64)] physical page of each logical
+ *                                             page; -1 = not resident
  *   union_cells  int32 [G][8*sel_cap]         out: ascending distinct cells of
  *                                             group g in [0, union_len[g])
  *   union_mask   uint8 [G][8*sel_cap]         out: bit i set iff query index
  *                                             8g+i chose the cell
+ *   union_rows   int32 [G][8*sel_cap]         out: the cell's pool row for KV
+ *                                             head 0, p * n_kv * 64 + c % 64
+ *                                             with p = page_table[c / 64]
+ *                                             (KV head h's row is that + 64 h,
+ *                                             in the [n_pages][n_kv][64] order
+ *                                             of the pools and scales); -1 when
+ *                                             the page is not resident
  *   union_len    int32 [G]                    out: size of group g's union
  *   status       uint32 [1]                   in/out: OR of SEL_ATTN_STATUS_*
- *   G = ceil(n_q / 8). Entries past union_len[g] are left untouched.
- *   Residency is not consulted: the union depends on the selections alone.
+ *   G = ceil(n_q / 8). Entries past union_len[g] are left untouched. The cells
+ *   and masks depend on the selections alone; only the rows read the table.
  *   Errors: a cell outside [0, n_ctx) is dropped and sets CELL_RANGE; a length
- *   outside [0, sel_cap] is clamped and sets SEL_LEN.
+ *   outside [0, sel_cap] is clamped and sets SEL_LEN; a page-table entry of a
+ *   union cell outside [-1, n_pages) sets PAGE_RANGE and gives row -1.
  *   Alignment: 4 bytes for the int32 arrays.
  */
 int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32_t* sel_len,
-                         int32_t* union_cells, uint8_t* union_mask, int32_t* union_len,
-                         uint32_t* status, hipStream_t stream);
+                         const int32_t* page_table, int32_t* union_cells, uint8_t* union_mask,
+                         int32_t* union_rows, int32_t* union_len, uint32_t* status,
+                         hipStream_t stream);
 
 /*
  * sel_attn_prefill - the attention step over each group's union (section
  * Summary: INT8 K/V of 64-cell chunks of the union dequantised once, S^T = K Q^T
  * and O += P V on matrix cores with FP32 sums for the group's 96 rows, cells the
  * row's position did not choose set to -inf in the online softmax; section
- * What changed: one work-group per group of 8 positions and KV head).
+ * What changed: one work-group per group of 8 positions and KV head; section
+ * Extra Notes: cells of pages that are not resident are masked for everyone).
  *
  *   q            const float [n_q][n_kv*12][128]        queries (rounded to
  *                                                       FP16 for the products)
@@ -167,13 +183,11 @@ int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32
  *   v_pool       const int8  [n_pages][n_kv][64][128]   KV head, cell, dim
  *   k_scale      const float [n_pages][n_kv][64]        per cell and KV head:
  *   v_scale      const float [n_pages][n_kv][64]        k = k_int8 * k_scale
- *   page_table   const int32 [ceil(n_ctx/64)]           physical page of each
- *                                                       logical page; -1 = not
- *                                                       resident (its cells are
- *                                                       masked for everyone)
- *   union_cells, union_mask, union_len                  as written by
+ *   union_rows, union_mask, union_len                   as written by
  *                                                       sel_attn_build_union
- *                                                       with the same dims
+ *                                                       with the same dims; a
+ *                                                       row of -1 is masked for
+ *                                                       everyone
  *   softmax_scale                                       multiplies q.k (e.g.
  *                                                       1/sqrt(128))
  *   out          float [n_q][n_kv*12][128]              out: softmax-weighted
@@ -188,15 +202,17 @@ int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32
  *   as an FP16 factor (v_scale * 2^6) on the FP16 probability.
  *   Supported scales: |v_scale| < 4 (other values set V_SCALE); k_scale any
  *   finite value.
- *   Errors: CELL_RANGE, PAGE_RANGE, UNION_LEN, V_SCALE as listed above; a bad
- *   cell or page is treated as not resident.
+ *   Errors: UNION_LEN and V_SCALE as listed above; PAGE_RANGE for a row r
+ *   other than -1 whose KV-head rows r + 64 h would leave the pools
+ *   (r < 0 or r >= (n_pages * n_kv - n_kv + 1) * 64), and such a cell is
+ *   treated as not resident. A row inside that range is read as given.
  *   Alignment: q, out, k_pool, v_pool 16 bytes; the rest 4 bytes (mask 1).
  */
 int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
                      const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                     const int32_t* page_table, const int32_t* union_cells,
-                     const uint8_t* union_mask, const int32_t* union_len,
-                     float softmax_scale, float* out, uint32_t* status, hipStream_t stream);
+                     const int32_t* union_rows, const uint8_t* union_mask,
+                     const int32_t* union_len, float softmax_scale, float* out, uint32_t* status,
+                     hipStream_t stream);
 
 /*
  * sel_attn_prefill_workspace_bytes - device workspace that sel_attn_prefill_split
@@ -229,10 +245,10 @@ size_t sel_attn_prefill_workspace_bytes(const sel_attn_dims* d);
  */
 int sel_attn_prefill_split(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
                            const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                           const int32_t* page_table, const int32_t* union_cells,
-                           const uint8_t* union_mask, const int32_t* union_len,
-                           float softmax_scale, float* out, uint32_t* status, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream);
+                           const int32_t* union_rows, const uint8_t* union_mask,
+                           const int32_t* union_len, float softmax_scale, float* out,
+                           uint32_t* status, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * sel_attn_prefill_positions - the same attention as sel_attn_build_union +
@@ -243,8 +259,10 @@ int sel_attn_prefill_split(const sel_attn_dims* d, const float* q, const int8_t*
  * selections share cells, and gains nothing when they are unrelated). Pick this call
  * when the union of 8 neighbours is several times one selection.
  *
- *   q, k_pool, v_pool, k_scale, v_scale, page_table, softmax_scale, out,
- *   status      as for sel_attn_prefill
+ *   q, k_pool, v_pool, k_scale, v_scale, softmax_scale, out, status
+ *                as for sel_attn_prefill
+ *   page_table   const int32 [ceil(n_ctx/64)]: physical page of each logical
+ *                page; -1 = not resident
  *   sel, sel_len as for sel_attn_build_union: any order, repeats count once
  *   Precision: the products take Q, K, V and P' = p * v_scale * 2^6 in FP16
  *   (round to nearest even); scores, softmax and sums are FP32. Results agree

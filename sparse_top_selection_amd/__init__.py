@@ -79,14 +79,14 @@ def make_dims(n_ctx: int, n_q: int, n_kv: int, n_pages: int, sel_cap: int = 2051
 _p = ctypes.c_void_p
 _lib.sel_attn_select_blocks.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32, _p, _p, _p, _p]
 _lib.sel_attn_select_blocks.restype = ctypes.c_int
-_lib.sel_attn_build_union.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p]
+_lib.sel_attn_build_union.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p]
 _lib.sel_attn_build_union.restype = ctypes.c_int
-_lib.sel_attn_prefill.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p,
+_lib.sel_attn_prefill.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
                                   ctypes.c_float, _p, _p, _p]
 _lib.sel_attn_prefill.restype = ctypes.c_int
 _lib.sel_attn_prefill_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
 _lib.sel_attn_prefill_workspace_bytes.restype = ctypes.c_size_t
-_lib.sel_attn_prefill_split.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p, _p,
+_lib.sel_attn_prefill_split.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
                                         ctypes.c_float, _p, _p, _p, ctypes.c_size_t, _p]
 _lib.sel_attn_prefill_split.restype = ctypes.c_int
 _lib.sel_attn_prefill_positions.argtypes = [ctypes.POINTER(Dims), _p, _p, _p, _p, _p, _p, _p, _p,
@@ -142,21 +142,21 @@ def sel_attn_select_blocks(dims: Dims, first_pos: int, block_scores, sel, sel_le
                                        _ptr(sel), _ptr(sel_len), _stream(stream)))
 
 
-def sel_attn_build_union(dims: Dims, sel, sel_len, union_cells, union_mask, union_len, status,
-                         stream=None) -> None:
+def sel_attn_build_union(dims: Dims, sel, sel_len, page_table, union_cells, union_mask, union_rows,
+                         union_len, status, stream=None) -> None:
     """Enqueue the union step (see include/sel_attn.h). Tensors or raw device pointers."""
     _check(_lib.sel_attn_build_union(ctypes.byref(dims), _ptr(sel), _ptr(sel_len),
-                                     _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
-                                     _ptr(status), _stream(stream)))
+                                     _ptr(page_table), _ptr(union_cells), _ptr(union_mask),
+                                     _ptr(union_rows), _ptr(union_len), _ptr(status),
+                                     _stream(stream)))
 
 
-def sel_attn_prefill(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
-                     union_mask, union_len, softmax_scale: float, out, status,
-                     stream=None) -> None:
+def sel_attn_prefill(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, union_rows, union_mask,
+                     union_len, softmax_scale: float, out, status, stream=None) -> None:
     """Enqueue the attention step (see include/sel_attn.h). Tensors or raw device pointers."""
     _check(_lib.sel_attn_prefill(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-                                 _ptr(k_scale), _ptr(v_scale), _ptr(page_table),
-                                 _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(union_rows),
+                                 _ptr(union_mask), _ptr(union_len),
                                  ctypes.c_float(float(softmax_scale)), _ptr(out), _ptr(status),
                                  _stream(stream)))
 
@@ -166,14 +166,14 @@ def sel_attn_prefill_workspace_bytes(dims: Dims) -> int:
     return int(_lib.sel_attn_prefill_workspace_bytes(ctypes.byref(dims)))
 
 
-def sel_attn_prefill_split(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, page_table,
-                           union_cells, union_mask, union_len, softmax_scale: float, out, status,
-                           workspace, workspace_bytes: int, stream=None) -> None:
+def sel_attn_prefill_split(dims: Dims, q, k_pool, v_pool, k_scale, v_scale, union_rows,
+                           union_mask, union_len, softmax_scale: float, out, status, workspace,
+                           workspace_bytes: int, stream=None) -> None:
     """Enqueue the attention step, splitting small grids over the workspace (see
     include/sel_attn.h). Tensors or raw device pointers."""
     _check(_lib.sel_attn_prefill_split(ctypes.byref(dims), _ptr(q), _ptr(k_pool), _ptr(v_pool),
-                                       _ptr(k_scale), _ptr(v_scale), _ptr(page_table),
-                                       _ptr(union_cells), _ptr(union_mask), _ptr(union_len),
+                                       _ptr(k_scale), _ptr(v_scale), _ptr(union_rows),
+                                       _ptr(union_mask), _ptr(union_len),
                                        ctypes.c_float(float(softmax_scale)), _ptr(out),
                                        _ptr(status), _ptr(workspace), ctypes.c_size_t(workspace_bytes),
                                        _stream(stream)))
@@ -302,32 +302,43 @@ def select_blocks(block_scores: torch.Tensor, first_pos: int, n_ctx: int,
     return sel, sel_len
 
 
-def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, status=None, stream=None,
-                out=None):
-    """Union of every group of 8 query indices. Returns (cells, mask, length, status)."""
+def build_union(sel: torch.Tensor, sel_len: torch.Tensor, n_ctx: int, page_table=None,
+                n_kv: int = 1, n_pages: int = 1, status=None, stream=None, out=None):
+    """Union of every group of 8 query indices, each cell also resolved through
+    the page table to its pool row for KV head 0 (pools [n_pages][n_kv][64][128]).
+    Without a page table every page counts as not resident (rows -1); the cells
+    and masks do not depend on it. Returns (cells, mask, rows, length, status)."""
     dev = _on_gpu(sel, "sel")
     _need(sel, "sel", torch.int32, 2, dev)
     _need(sel_len, "sel_len", torch.int32, 1, dev)
     n_q, cap = sel.shape
     if sel_len.shape[0] != n_q:
         raise ValueError("sel_len must have n_q entries")
+    n_lpages = -(-n_ctx // PAGE_SIZE)
+    if page_table is None:
+        page_table = torch.full((n_lpages,), -1, dtype=torch.int32, device=dev)
+    _need(page_table, "page_table", torch.int32, 1, dev)
+    if page_table.shape[0] < n_lpages:
+        raise ValueError("page_table needs ceil(n_ctx / page_size) entries")
     g = (n_q + 7) // 8
     if out is None:
         cells = torch.empty((g, 8 * cap), dtype=torch.int32, device=dev)
         mask = torch.empty((g, 8 * cap), dtype=torch.uint8, device=dev)
+        rows = torch.empty((g, 8 * cap), dtype=torch.int32, device=dev)
         length = torch.empty(g, dtype=torch.int32, device=dev)
     else:
-        cells, mask, length = out
+        cells, mask, rows, length = out
         _need_shape(cells, "union_cells", torch.int32, (g, 8 * cap), dev)
         _need_shape(mask, "union_mask", torch.uint8, (g, 8 * cap), dev)
+        _need_shape(rows, "union_rows", torch.int32, (g, 8 * cap), dev)
         _need_shape(length, "union_len", torch.int32, (g,), dev)
     status = _status_for(status, dev)
-    dims = make_dims(n_ctx, n_q, 1, 1, sel_cap=cap)
-    sel_attn_build_union(dims, sel, sel_len, cells, mask, length, status, stream)
-    return cells, mask, length, status
+    dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=cap)
+    sel_attn_build_union(dims, sel, sel_len, page_table, cells, mask, rows, length, status, stream)
+    return cells, mask, rows, length, status
 
 
-def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_mask, union_len,
+def prefill(q, k_pool, v_pool, k_scale, v_scale, union_rows, union_mask, union_len,
             softmax_scale: float, n_ctx: int, status=None, stream=None, out=None, split=False,
             workspace=None):
     """Attention over each group's union. With split=True, grids too small for
@@ -338,8 +349,7 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
     for name, t, dt, nd in (("k_pool", k_pool, torch.int8, 4), ("v_pool", v_pool, torch.int8, 4),
                             ("k_scale", k_scale, torch.float32, 3),
                             ("v_scale", v_scale, torch.float32, 3),
-                            ("page_table", page_table, torch.int32, 1),
-                            ("union_cells", union_cells, torch.int32, 2),
+                            ("union_rows", union_rows, torch.int32, 2),
                             ("union_mask", union_mask, torch.uint8, 2),
                             ("union_len", union_len, torch.int32, 1)):
         _need(t, name, dt, nd, dev)
@@ -350,13 +360,11 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
         raise ValueError("pool / scale shapes disagree")
     if hd2 != hd or n_qh != n_kv * Q_PER_KV:
         raise ValueError("q is [n_q][n_kv*12][head_dim] with the pools' n_kv and head_dim")
-    if page_table.shape[0] < -(-n_ctx // ps):
-        raise ValueError("page_table needs ceil(n_ctx / page_size) entries")
     g = (n_q + 7) // 8
-    if union_len.shape[0] != g or union_cells.shape[0] != g or union_cells.shape[1] % 8 != 0 \
-            or union_mask.shape != union_cells.shape:
+    if union_len.shape[0] != g or union_rows.shape[0] != g or union_rows.shape[1] % 8 != 0 \
+            or union_mask.shape != union_rows.shape:
         raise ValueError("union arrays must be [ceil(n_q/8)][8*sel_cap]")
-    cap = union_cells.shape[1] // 8
+    cap = union_rows.shape[1] // 8
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -364,16 +372,16 @@ def prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells, union_
     status = _status_for(status, dev)
     dims = make_dims(n_ctx, n_q, n_kv, n_pages, sel_cap=cap, head_dim=hd, page_size=ps)
     if not split:
-        sel_attn_prefill(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
-                         union_mask, union_len, softmax_scale, out, status, stream)
+        sel_attn_prefill(dims, q, k_pool, v_pool, k_scale, v_scale, union_rows, union_mask,
+                         union_len, softmax_scale, out, status, stream)
         return out, status
     need = sel_attn_prefill_workspace_bytes(dims)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, 1, dev)
-    sel_attn_prefill_split(dims, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
-                           union_mask, union_len, softmax_scale, out, status, workspace,
+    sel_attn_prefill_split(dims, q, k_pool, v_pool, k_scale, v_scale, union_rows, union_mask,
+                           union_len, softmax_scale, out, status, workspace,
                            workspace.numel() * workspace.element_size(), stream)
     return out, status
 
@@ -439,9 +447,13 @@ def decode(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len, softma
 
 
 def attention(q, k_pool, v_pool, k_scale, v_scale, page_table, sel, sel_len,
-              softmax_scale: float, n_ctx: int, stream=None):
-    """One pass of the whole path (union, then attention). Returns (out, union, status)."""
-    cells, mask, length, status = build_union(sel, sel_len, n_ctx, stream=stream)
-    out, status = prefill(q, k_pool, v_pool, k_scale, v_scale, page_table, cells, mask, length,
-                          softmax_scale, n_ctx, status=status, stream=stream)
-    return out, (cells, mask, length), status
+              softmax_scale: float, n_ctx: int, stream=None, split=False):
+    """One pass of the whole path (union, then attention). Returns
+    (out, (cells, mask, rows, length), status)."""
+    _need(k_pool, "k_pool", torch.int8, 4, _on_gpu(k_pool, "k_pool"))
+    n_pages, n_kv = k_pool.shape[0], k_pool.shape[1]
+    cells, mask, rows, length, status = build_union(sel, sel_len, n_ctx, page_table, n_kv, n_pages,
+                                                    stream=stream)
+    out, status = prefill(q, k_pool, v_pool, k_scale, v_scale, rows, mask, length, softmax_scale,
+                          n_ctx, status=status, stream=stream, split=split)
+    return out, (cells, mask, rows, length), status

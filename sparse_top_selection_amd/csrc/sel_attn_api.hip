@@ -129,8 +129,9 @@ int sel_attn_select_blocks(const sel_attn_dims* d, int32_t first_pos, const floa
 }
 
 int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32_t* sel_len,
-                         int32_t* union_cells, uint8_t* union_mask, int32_t* union_len,
-                         uint32_t* status, hipStream_t stream) {
+                         const int32_t* page_table, int32_t* union_cells, uint8_t* union_mask,
+                         int32_t* union_rows, int32_t* union_len, uint32_t* status,
+                         hipStream_t stream) {
   static const char* who = "sel_attn_build_union";
   int rc = check_dims(d, who);
   if (rc) return rc;
@@ -139,23 +140,28 @@ int sel_attn_build_union(const sel_attn_dims* d, const int32_t* sel, const int32
     g_err[0] = 0;
     return SEL_ATTN_OK;
   }
-  if (!sel || !sel_len || !union_cells || !union_mask || !union_len)
+  if (!sel || !sel_len || !page_table || !union_cells || !union_mask || !union_rows || !union_len)
     return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
-  if (!aligned(sel, 4) || !aligned(sel_len, 4) || !aligned(union_cells, 4) ||
-      !aligned(union_len, 4) || !aligned(status, 4))
+  if (!aligned(sel, 4) || !aligned(sel_len, 4) || !aligned(page_table, 4) ||
+      !aligned(union_cells, 4) || !aligned(union_rows, 4) || !aligned(union_len, 4) ||
+      !aligned(status, 4))
     return fail(SEL_ATTN_EINVAL, "%s: int32 arrays must be 4-byte aligned", who);
   rc = check_device(who);
   if (rc) return rc;
   selattn::UnionArgs a;
   a.sel = sel;
   a.sel_len = sel_len;
+  a.page_table = page_table;
   a.union_cells = union_cells;
   a.union_mask = union_mask;
+  a.union_rows = union_rows;
   a.union_len = union_len;
   a.status = status;
   a.n_ctx = d->n_ctx;
   a.n_q = d->n_q;
   a.sel_cap = d->sel_cap;
+  a.n_kv = d->n_kv;
+  a.n_pages = d->n_pages;
   hipError_t e = selattn::launch_union_build(a, stream);
   if (e != hipSuccess) return fail(SEL_ATTN_ELAUNCH, "%s: launch: %s", who, hipGetErrorString(e));
   g_err[0] = 0;
@@ -177,9 +183,9 @@ int64_t prefill_max_cells(const sel_attn_dims* d) {
 // arguments (one work-group per (group, KV head) and split).
 int prefill_args(const sel_attn_dims* d, const char* who, const float* q, const int8_t* k_pool,
                  const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                 const int32_t* page_table, const int32_t* union_cells, const uint8_t* union_mask,
-                 const int32_t* union_len, float softmax_scale, float* out, uint32_t* status,
-                 selattn::PrefillArgs& a, void* workspace = nullptr, size_t workspace_bytes = 0,
+                 const int32_t* union_rows, const uint8_t* union_mask, const int32_t* union_len,
+                 float softmax_scale, float* out, uint32_t* status, selattn::PrefillArgs& a,
+                 void* workspace = nullptr, size_t workspace_bytes = 0,
                  bool split = false) {
   int rc = check_dims(d, who);
   if (rc) return rc;
@@ -187,13 +193,13 @@ int prefill_args(const sel_attn_dims* d, const char* who, const float* q, const 
   if (!isfinite(softmax_scale))
     return fail(SEL_ATTN_EINVAL, "%s: softmax_scale must be finite", who);
   if (d->n_q == 0) return 0;
-  if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !page_table || !union_cells ||
-      !union_mask || !union_len || !out)
+  if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !union_rows || !union_mask ||
+      !union_len || !out)
     return fail(SEL_ATTN_EINVAL, "%s: NULL array pointer", who);
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
     return fail(SEL_ATTN_EINVAL, "%s: q, out, k_pool and v_pool must be 16-byte aligned", who);
-  if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(page_table, 4) ||
-      !aligned(union_cells, 4) || !aligned(union_len, 4) || !aligned(status, 4))
+  if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(union_rows, 4) ||
+      !aligned(union_len, 4) || !aligned(status, 4))
     return fail(SEL_ATTN_EINVAL, "%s: scale and int32 arrays must be 4-byte aligned", who);
   const int64_t items = (int64_t)((d->n_q + 7) / 8) * d->n_kv;
   const int splits = split ? selattn::prefill_split_count(items, prefill_max_cells(d)) : 1;
@@ -212,8 +218,7 @@ int prefill_args(const sel_attn_dims* d, const char* who, const float* q, const 
   a.v_pool = v_pool;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  a.page_table = page_table;
-  a.union_cells = union_cells;
+  a.union_rows = union_rows;
   a.union_mask = union_mask;
   a.union_len = union_len;
   a.out = out;
@@ -223,6 +228,9 @@ int prefill_args(const sel_attn_dims* d, const char* who, const float* q, const 
   a.n_q = d->n_q;
   a.n_kv = d->n_kv;
   a.n_pages = d->n_pages;
+  // a row r is read for KV heads 0..n_kv-1 at r + 64 h: inside the pools while
+  // r < (n_pages n_kv - n_kv + 1) 64 (check_dims keeps the product in range)
+  a.row_limit = (uint32_t)(((int64_t)d->n_pages * d->n_kv - d->n_kv + 1) * SEL_ATTN_PAGE_SIZE);
   a.sel_cap = d->sel_cap;
   a.n_groups = (d->n_q + 7) / 8;
   a.n_splits = splits;
@@ -238,13 +246,13 @@ extern "C" {
 
 int sel_attn_prefill(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
                      const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                     const int32_t* page_table, const int32_t* union_cells,
-                     const uint8_t* union_mask, const int32_t* union_len, float softmax_scale,
-                     float* out, uint32_t* status, hipStream_t stream) {
+                     const int32_t* union_rows, const uint8_t* union_mask,
+                     const int32_t* union_len, float softmax_scale, float* out, uint32_t* status,
+                     hipStream_t stream) {
   static const char* who = "sel_attn_prefill";
   selattn::PrefillArgs a;
-  int rc = prefill_args(d, who, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
-                        union_mask, union_len, softmax_scale, out, status, a);
+  int rc = prefill_args(d, who, q, k_pool, v_pool, k_scale, v_scale, union_rows, union_mask,
+                        union_len, softmax_scale, out, status, a);
   if (rc) return rc;
   if (d->n_q == 0) {
     g_err[0] = 0;
@@ -265,15 +273,15 @@ size_t sel_attn_prefill_workspace_bytes(const sel_attn_dims* d) {
 
 int sel_attn_prefill_split(const sel_attn_dims* d, const float* q, const int8_t* k_pool,
                            const int8_t* v_pool, const float* k_scale, const float* v_scale,
-                           const int32_t* page_table, const int32_t* union_cells,
-                           const uint8_t* union_mask, const int32_t* union_len,
-                           float softmax_scale, float* out, uint32_t* status, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+                           const int32_t* union_rows, const uint8_t* union_mask,
+                           const int32_t* union_len, float softmax_scale, float* out,
+                           uint32_t* status, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   static const char* who = "sel_attn_prefill_split";
   selattn::PrefillArgs a;
-  int rc = prefill_args(d, who, q, k_pool, v_pool, k_scale, v_scale, page_table, union_cells,
-                        union_mask, union_len, softmax_scale, out, status, a, workspace,
-                        workspace_bytes, true);
+  int rc = prefill_args(d, who, q, k_pool, v_pool, k_scale, v_scale, union_rows, union_mask,
+                        union_len, softmax_scale, out, status, a, workspace, workspace_bytes,
+                        true);
   if (rc) return rc;
   if (d->n_q == 0) {
     g_err[0] = 0;

@@ -11,13 +11,17 @@ namespace selattn {
 struct UnionArgs {
   const int32_t* sel;
   const int32_t* sel_len;
+  const int32_t* page_table;
   int32_t* union_cells;
   uint8_t* union_mask;
+  int32_t* union_rows;   // pool row of each union cell for KV head 0, -1 if not resident
   int32_t* union_len;
   uint32_t* status;
   int32_t n_ctx;
   int32_t n_q;
   int32_t sel_cap;
+  int32_t n_kv;
+  int32_t n_pages;
 };
 
 struct PrefillArgs {
@@ -26,8 +30,7 @@ struct PrefillArgs {
   const int8_t* v_pool;
   const float* k_scale;
   const float* v_scale;
-  const int32_t* page_table;
-  const int32_t* union_cells;
+  const int32_t* union_rows;
   const uint8_t* union_mask;
   const int32_t* union_len;
   float* out;
@@ -37,6 +40,7 @@ struct PrefillArgs {
   int32_t n_q;
   int32_t n_kv;
   int32_t n_pages;
+  uint32_t row_limit;  // union rows r with r + 64 (n_kv - 1) inside the pools: r < row_limit
   int32_t sel_cap;
   int32_t n_groups;
   int32_t per_xcd;     // workgroups each XCD walks through (grid = 8 * per_xcd)

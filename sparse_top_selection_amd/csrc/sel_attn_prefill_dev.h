@@ -13,7 +13,9 @@
 //     part in that position's softmax (its logit counts as -inf); both products
 //     take their operands (Q, K, V, P) in FP16.
 //   section What changed: one work-group per 8 positions and KV head.
-//   section Extra Notes: cells of non-resident pages are masked.
+//   section Extra Notes: cells of non-resident pages are masked (here the union
+//     carries each cell's pool row, resolved through the page table once per
+//     cell when the union is built, instead of once per KV head here).
 //
 // gfx950 mapping (the page's 16-lane sub-group / 256-GRF shape is Xe2 prior art
 // and is not reproduced):
@@ -22,14 +24,15 @@
 //     loop) per (group g, KV head h); grid order is XCD-aware so that each XCD
 //     walks consecutive groups of one KV head;
 //   * waves 0..2 consume, wave 3 produces (at raised priority: every wave waits
-//     for its stage at the barrier). The producer translates union cells
-//     through the page table (two chunks at a time, every other iteration) and
-//     gathers the INT8 K/V rows with 16-byte loads, every read consumed at
-//     least kLead iterations after it was issued, converts the rows to FP16
-//     and stores them into LDS (K tiles in two stages, V tiles and per-cell
-//     factors in four); a chunk's V tile and factors are stored one iteration
-//     after its K tile, at the start of an iteration, so that only the K
-//     stores are waited for at the barrier; the consumers only read LDS;
+//     for its stage at the barrier). The producer turns the union's pool rows
+//     into this KV head's offsets (two chunks at a time, every other
+//     iteration) and gathers the INT8 K/V rows with 16-byte loads, every read
+//     consumed at least kLead iterations after it was issued, converts the
+//     rows to FP16 and stores them into LDS (K tiles in two stages, V tiles
+//     and per-cell factors in four); a chunk's V tile and factors are stored
+//     one iteration after its K tile, at the start of an iteration, so that
+//     only the K stores are waited for at the barrier; the consumers only
+//     read LDS;
 //   * row n of the 96 = 8*hq + i (query head h*12+hq, position 8g+i), so the
 //     chooser bit of row n is n & 7; consumer wave w owns row block w (32 rows)
 //     and every cell of each chunk, with its own softmax state;
@@ -227,62 +230,45 @@ __device__ __forceinline__ void store_v_task(const Stage& st, int t, u32x4 raw) 
 }
 
 // ---------------------------------------------------------------------------
-// Page translation of one chunk cell (one lane per cell; the two lane halves
-// take the two chunks of a pair), in three steps whose global reads are each
-// consumed four iterations after they were issued (at least the lead of the
-// K/V gathers, so that no wait for an early read also waits for gathers still
-// in flight): read the union entry, then the page-table entry, then form the
-// pool row and publish it in the ring.
+// Translation of one chunk cell (one lane per cell; the two lane halves take
+// the two chunks of a pair), in two steps: read the union entry (the cell's
+// pool row for KV head 0, resolved through the page table when the union was
+// built, and its chooser byte), then, four iterations later (at least the lead
+// of the K/V gathers, so that no wait for an early read also waits for gathers
+// still in flight), form this KV head's pool offset and publish it in the ring.
 // Records carry only loaded words (each in a register of its own: packing a
 // field next to another would read the in-flight load at once); whether an
 // entry lies inside the union is recomputed from the chunk index.
 struct UnionRec {
-  int32_t cell;
+  int32_t row;
   uint32_t mask;
-};
-
-struct PageRec {
-  int32_t cell;
-  uint32_t mask;
-  int32_t page_raw;   // page_table entry (of page 0 when the cell is not in [0, n_ctx))
 };
 
 __device__ __forceinline__ bool in_union(int U, int cc, int lane) { return cc * kChunk + lane < U; }
 
-// All steps are branch-free (clamped, always-valid addresses plus selects) so
+// Both steps are branch-free (clamped, always-valid addresses plus selects) so
 // that a producer iteration stays one basic block.
 __device__ __forceinline__ UnionRec read_union_entry(const PrefillArgs& a, int64_t ubase, int U,
                                                      int cc, int lane) {
   // union rows hold at least 8 entries, so index 0 is always readable
   const int64_t at = ubase + (in_union(U, cc, lane) ? cc * kChunk + lane : 0);
   UnionRec u;
-  u.cell = a.union_cells[at];
+  u.row = a.union_rows[at];
   u.mask = a.union_mask[at];
   return u;
 }
 
-__device__ __forceinline__ PageRec read_page_entry(const PrefillArgs& a, const UnionRec& u) {
-  PageRec p;
-  p.cell = u.cell;
-  p.mask = u.mask;
-  const bool in_ctx = u.cell >= 0 && u.cell < a.n_ctx;
-  p.page_raw = a.page_table[in_ctx ? (u.cell >> 6) : 0];
-  return p;
-}
-
-__device__ __forceinline__ void finish_translation(const PrefillArgs& a, const PageRec& p, int U,
+// A row of -1 is a page that is not resident; a row whose KV-head rows would
+// leave the pools is flagged and treated the same way.
+__device__ __forceinline__ void finish_translation(const PrefillArgs& a, const UnionRec& u, int U,
                                                    int cc, int h, Ring& rg, int lane,
                                                    uint32_t& flags) {
   const bool valid = in_union(U, cc, lane);
-  const bool in_ctx = valid && p.cell >= 0 && p.cell < a.n_ctx;
-  const int32_t page = in_ctx ? p.page_raw : -1;
-  const bool cell_bad = valid && !in_ctx;
-  const bool page_bad = in_ctx && (page >= a.n_pages || page < -1);
-  flags |= (cell_bad ? SEL_ATTN_STATUS_CELL_RANGE : 0u) | (page_bad ? SEL_ATTN_STATUS_PAGE_RANGE : 0u);
-  const bool usable = in_ctx && !page_bad && page >= 0;
-  const uint32_t row = (uint32_t)((page * a.n_kv + h) * 64 + (p.cell & 63));
+  const bool usable = valid && (uint32_t)u.row < a.row_limit;
+  flags |= (valid && u.row != -1 && !usable) ? SEL_ATTN_STATUS_PAGE_RANGE : 0u;
+  const uint32_t row = (uint32_t)u.row + 64u * (uint32_t)h;
   rg.off[lane] = usable ? row * kD : 0u;
-  rg.mask[lane] = (uint8_t)(usable ? p.mask : 0u);
+  rg.mask[lane] = (uint8_t)(usable ? u.mask : 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -628,9 +614,9 @@ __device__ __forceinline__ void consume(const PrefillArgs& a, Smem& sm, int g, i
 // ---------------------------------------------------------------------------
 // Producer wave 3 (64 threads, ptid = tid - 192). Iteration c (while the
 // consumers work on chunks c and c+1): store chunk c+1's V tile and factors,
-// on even c translate a pair of chunks (union entries of c+14, c+15, page-table
-// entries of c+10, c+11, ring slots of c+6, c+7; lane half hb takes the pair's
-// chunk hb, cell ptid & 31), gather chunk c+kAheadGather into registers (its
+// on even c translate a pair of chunks (union entries of c+10, c+11 read, ring
+// slots of c+6, c+7 written; lane half hb takes the pair's chunk hb, cell
+// ptid & 31), gather chunk c+kAheadGather into registers (its
 // ring slot read at the end of the previous iteration), store the K tile of
 // chunk c+2 (gathered kLead iterations earlier) and read the ring slot of the
 // next iteration's gather. Each
@@ -719,28 +705,27 @@ __device__ __forceinline__ void convert_v(const PrefillArgs& a, const Stage& st,
   *reinterpret_cast<uint2*>(kp) = keep_words(r.kw, ptid & 7);
 }
 
-// Producer state, each array indexed by chunk & 3: gathered rows (chunk x is
-// gathered in iteration x-2-kLead and converted in x-2), union records (read in
-// x-4-3*kLead, consumed in x-4-2*kLead) and page records (read then, consumed
-// in x-4-kLead, when the ring slot of chunk x is written). Every index below is
-// a compile-time constant once a step is instantiated for its phase P = c & 3,
-// so the sets stay in registers and the stage addresses fold into immediates.
+// Producer state: gathered rows, indexed by chunk & 3 (chunk x is gathered in
+// iteration x-2-kLead and converted in x-2), and union records (read four
+// iterations before the ring slots of their chunks are written). Every index
+// below is a compile-time constant once a step is instantiated for its phase
+// P = c & 3, so the sets stay in registers and the stage addresses fold into
+// immediates.
 constexpr int kAheadGather = 2 + kLead;        // chunk gathered in iteration c: c + 5
 // Translation runs on even iterations c, for a pair of chunks at once (lane
-// half hb takes chunk 2m + hb of pair m): the ring slots of pair c+6, c+7 are
-// written from page records read four iterations earlier, whose union records
-// were read four iterations before that. Chunk x's slot is thus written one or
-// two iterations before x is gathered (x - 5).
+// half hb takes chunk c' + hb of the pair starting at c'): the ring slots of
+// chunks c+6, c+7 are written from union records read four iterations earlier.
+// Chunk x's slot is thus written one or two iterations before x is gathered
+// (x - 5).
 constexpr int kPairFinish = 6;                 // pair whose ring slots are written: c + 6, c + 7
-constexpr int kPairPage = 10;                  // pair whose page entries are read: c + 10, c + 11
-constexpr int kPairUnion = 14;                 // pair whose union entries are read: c + 14, c + 15
+constexpr int kPairUnion = 10;                 // pair whose union entries are read: c + 10, c + 11
 static_assert(kAheadGather < kPairFinish && kPairFinish + 1 < kAheadGather + kRing,
               "ring slots are written before their gather and kept until it");
+static_assert(kPairUnion == kPairFinish + 4, "union records are consumed four iterations later");
 
 struct ProdState {
   Raw raw[4];
-  UnionRec un[2];   // by pair parity
-  PageRec pg[2];
+  UnionRec un[2];   // by phase: set P / 2 is read and consumed in phase P (0 or 2)
   GatherAddr ga;    // ring reads of the next iteration's gather
 };
 
@@ -748,8 +733,8 @@ struct ProdState {
 // It opens with the V tile and factors of chunk c+1, so that those stores drain
 // while the rest of the iteration runs, and closes with the K tile of chunk c+2,
 // the only stores the consumers need right after this iteration's barrier.
-// Reads are issued page, union, gather; translation reads are consumed four
-// iterations later, gathers kLead; the gather of chunk c+5 reuses the register
+// Reads are issued union, gather; union records are consumed four iterations
+// later, gathers kLead; the gather of chunk c+5 reuses the register
 // set that chunk c+1's V conversion has just emptied. `lower` (ptid < 32): this
 // lane stores k factors, else v factors.
 template <int P>
@@ -759,13 +744,12 @@ __device__ __forceinline__ void produce_step(const PrefillArgs& a, Smem& sm, Pro
   const int lane = ptid & (kChunk - 1);
   convert_v(a, stage(sm, P + 1), ptid, lower, ps.raw[(P + 1) & 3], flags);
   if constexpr ((P & 1) == 0) {
-    // pairs c/2 + 3, + 5 and + 7 share a parity: each record set is consumed
-    // before it is refilled
-    constexpr int s = (P / 2 + 1) & 1;
+    // the record set of this phase was read four iterations ago for the pair
+    // finished now, and is refilled for the one finished four iterations on
+    constexpr int s = P / 2;
     const int hb = ptid >> 5;
     const int cf = c + kPairFinish + hb;
-    finish_translation(a, ps.pg[s], U, cf, h, sm.ring[cf & (kRing - 1)], lane, flags);
-    ps.pg[s] = read_page_entry(a, ps.un[s]);
+    finish_translation(a, ps.un[s], U, cf, h, sm.ring[cf & (kRing - 1)], lane, flags);
     ps.un[s] = read_union_entry(a, ubase, U, c + kPairUnion + hb, lane);
   }
   gather(a, ps.ga, ptid, ps.raw[(P + kAheadGather) & 3]);
@@ -780,28 +764,23 @@ __device__ __forceinline__ void produce(const PrefillArgs& a, Smem& sm, int h, i
                                         int64_t ubase, int ptid, bool lower,
                                         uint32_t& flags) {
   static_assert(kLead >= 1 && kLead <= 3 && kStages == 4, "register sets cover the lead");
-  static_assert(kPairFinish == 6 && kPairPage == 10 && kPairUnion == 14, "the prologue below");
+  static_assert(kPairFinish == 6 && kPairUnion == 10, "the prologue below");
   const int lane = ptid & (kChunk - 1);
   const int hb = ptid >> 5;
   ProdState ps;
-  // prologue: what iteration 0 expects. Pairs 0..2 (chunks 0..5) translated
-  // into their ring slots; page records of pairs 3 and 4 and union records of
-  // pairs 5 and 6 read (sets by pair parity); chunk 0 staged, chunk 1's K tile
+  // prologue: what iteration 0 expects. Chunks 0..5 translated into their ring
+  // slots; the union records of chunks 6, 7 (set 0, finished in iteration 0)
+  // and 8, 9 (set 1, iteration 2) read; chunk 0 staged, chunk 1's K tile
   // staged, chunks 1 .. kAheadGather-1 gathered.
   {
-    UnionRec u[5];
+    UnionRec u[3];
 #pragma unroll
-    for (int m = 0; m < 5; ++m) u[m] = read_union_entry(a, ubase, U, 2 * m + hb, lane);
-    ps.un[1] = read_union_entry(a, ubase, U, 2 * 5 + hb, lane);
-    ps.un[0] = read_union_entry(a, ubase, U, 2 * 6 + hb, lane);
-    PageRec p[3];
-#pragma unroll
-    for (int m = 0; m < 3; ++m) p[m] = read_page_entry(a, u[m]);
-    ps.pg[1] = read_page_entry(a, u[3]);
-    ps.pg[0] = read_page_entry(a, u[4]);
+    for (int m = 0; m < 3; ++m) u[m] = read_union_entry(a, ubase, U, 2 * m + hb, lane);
+    ps.un[0] = read_union_entry(a, ubase, U, kPairFinish + hb, lane);
+    ps.un[1] = read_union_entry(a, ubase, U, kPairFinish + 2 + hb, lane);
 #pragma unroll
     for (int m = 0; m < 3; ++m)
-      finish_translation(a, p[m], U, 2 * m + hb, h, sm.ring[2 * m + hb], lane, flags);
+      finish_translation(a, u[m], U, 2 * m + hb, h, sm.ring[2 * m + hb], lane, flags);
   }
   lds_barrier();
   static_assert(kAheadGather == 5, "the prologue stages chunk 0 before gathering chunk 4");

@@ -1,11 +1,14 @@
 // Union builder: for each group of 8 adjacent query positions, one sorted list
 // of every cell any of them selected and, per entry, a byte whose bit i is set
-// when position i of the group selected that cell.
+// when position i of the group selected that cell, and the cell's pool row for
+// KV head 0 (its page-table entry resolved once here, not once per KV head by
+// the attention step).
 //
 // Page: #2808 "sycl: prompt attention over 8-query selection unions on XMX",
 // section Summary (the union and its marks) and section What changed (one
 // work-group per 8 positions, local bitmaps); section Extra Notes (a cell is an
-// int32, its mask a separate byte, so any context length works).
+// int32, its mask a separate byte, so any context length works; cells of pages
+// that are not resident are masked: their row is -1).
 //
 // gfx950 design: one 512-thread workgroup per group, four per CU (32 KiB of LDS
 // and at most 64 VGPRs each), so that the 1,024 groups of an 8,192-position
@@ -26,7 +29,9 @@
 //     256-cell slabs; an eight-entry prefix over the waves gives its output
 //     offset; then each nonempty slab is emitted 64 cells at a time (byte
 //     reads, ballot, mbcnt), so that consecutive lanes store consecutive union
-//     entries.
+//     entries. The 64 cells of one emission step lie in one logical page, so
+//     one page-table entry per step gives every lane's row; a wave's 64
+//     entries are read with one load, one per lane, before the counting pass.
 // Output order is ascending cell index, and the result is independent of row
 // order and repeats.
 
@@ -141,6 +146,9 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
   const int64_t ucap = 8LL * cap;
   int32_t* out_cells = a.union_cells + (int64_t)g * ucap;
   uint8_t* out_mask = a.union_mask + (int64_t)g * ucap;
+  int32_t* out_rows = a.union_rows + (int64_t)g * ucap;
+  const int last_page = (a.n_ctx - 1) >> 6;   // logical pages of the context: 0 .. last_page
+  const int kv_rows = 64 * a.n_kv;            // pool rows per physical page
 
   // the span: n_pos rows from sel + 8g * cap, read as the aligned 16-byte
   // blocks that overlap it; flat index f of a loaded entry = 4 * block - shift
@@ -216,6 +224,12 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
                         w0, win);
       }
     }
+    // this wave's share of the window covers logical pages pw .. pw + 63 (its
+    // 16 slabs of 256 cells): lane l reads entry pw + l now, and emission takes
+    // entry 4s + k of slab s, step k from that lane (clamped to the table; a
+    // page past the context holds no union cell)
+    const int pw = (w0 + 4 * wave * kWaveWords) >> 6;
+    const int32_t page_of_lane = a.page_table[min(pw + lane, last_page)];
     __syncthreads();
 
     // compaction of this wave's share of the window: words
@@ -248,6 +262,10 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
       const int s = __builtin_ctz(nonempty);
       nonempty &= nonempty - 1;
       const int rel0 = 4 * (wb + 64 * s) + lane;   // cell within the window, k = 0
+      // the 64 cells of step k are logical page pw + 4s + k, cell lane of it
+      int32_t pg[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pg[k] = __builtin_amdgcn_readlane(page_of_lane, 4 * s + k);
       uint32_t m[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) m[k] = bytes[rel0 + 64 * k];
@@ -257,8 +275,11 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
         if (m[k]) {
           const int at = o + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+          const bool resident = pg[k] >= 0 && pg[k] < a.n_pages;
+          flags |= (pg[k] < -1 || pg[k] >= a.n_pages) ? SEL_ATTN_STATUS_PAGE_RANGE : 0u;
           out_cells[at] = w0 + rel0 + 64 * k;
           out_mask[at] = (uint8_t)m[k];
+          out_rows[at] = resident ? pg[k] * kv_rows + lane : -1;
         }
         o += __builtin_popcountll(b);
       }

@@ -23,7 +23,7 @@ def run_path(problem: dict, dev: dict = None):
     """One pass: union then attention. Returns numpy (out, cells, mask, length, status)."""
     if dev is None:
         dev = to_device(problem)
-    out, (cells, mask, length), status = sa.attention(
+    out, (cells, mask, _, length), status = sa.attention(
         dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
         dev["page_table"], dev["sel"], dev["sel_len"], float(problem["softmax_scale"]),
         int(problem["n_ctx"]))
@@ -38,6 +38,12 @@ def assert_union_equal(cells, mask, length, ref):
     valid = np.arange(cells.shape[1])[None, :] < rl[:, None]
     bad = np.argwhere(valid & ((cells != rc) | (mask != rm)))
     assert bad.size == 0, "union differs at (group, index) %s" % (bad[:5].tolist(),)
+
+
+def assert_union_rows_equal(rows, length, ref_rows):
+    valid = np.arange(rows.shape[1])[None, :] < length[:, None]
+    bad = np.argwhere(valid & (rows != ref_rows))
+    assert bad.size == 0, "union rows differ at (group, index) %s" % (bad[:5].tolist(),)
 
 
 def error_stats(got: np.ndarray, ref: np.ndarray):

@@ -60,12 +60,11 @@ FAKE = 1 << 20   # never dereferenced: every case below fails on the host first
 def test_bad_dims_rejected_on_host(kw, code):
     import sparse_top_selection_amd as sa
     with pytest.raises(sa.SelAttnError) as e:
-        sa.sel_attn_build_union(_dims(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+        sa.sel_attn_build_union(_dims(**kw), *(FAKE,) * 8, stream=0)
     assert e.value.code == code
     assert "sel_attn_build_union" in sa.sel_attn_last_error()
     with pytest.raises(sa.SelAttnError) as e:
-        sa.sel_attn_prefill(_dims(**kw), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            0.1, FAKE, FAKE, stream=0)
+        sa.sel_attn_prefill(_dims(**kw), *(FAKE,) * 8, 0.1, FAKE, FAKE, stream=0)
     assert e.value.code == code
     with pytest.raises(sa.SelAttnError) as e:
         sa.sel_attn_select_blocks(_dims(sel_cap=2051, **kw) if "sel_cap" not in kw else _dims(**kw),
@@ -162,31 +161,40 @@ def test_decode_noalloc_rejects_on_host():
 
 def test_null_and_misaligned_pointers_rejected_on_host():
     import sparse_top_selection_amd as sa
-    with pytest.raises(sa.SelAttnError) as e:
-        sa.sel_attn_build_union(_dims(), FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
-    assert e.value.code == -1
-    with pytest.raises(sa.SelAttnError) as e:
-        sa.sel_attn_build_union(_dims(), FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
-    assert e.value.code == -1
+    # build_union: dims, sel, sel_len, page_table, cells, mask, rows, len, status
+    for bad in (1, 2, 3, 5, 6, 7):   # sel_len, page_table, cells, rows, len, status: NULL
+        args = [FAKE] * 8
+        args[bad] = None
+        with pytest.raises(sa.SelAttnError) as e:
+            sa.sel_attn_build_union(_dims(), *args, stream=0)
+        assert e.value.code == -1 and "NULL" in sa.sel_attn_last_error()
+    for bad in (0, 2, 5):      # sel, page_table, union_rows: 4-byte aligned
+        args = [FAKE] * 8
+        args[bad] = FAKE + 2
+        with pytest.raises(sa.SelAttnError) as e:
+            sa.sel_attn_build_union(_dims(), *args, stream=0)
+        assert e.value.code == -1 and "aligned" in sa.sel_attn_last_error()
     with pytest.raises(sa.SelAttnError) as e:   # q must be 16-byte aligned
-        sa.sel_attn_prefill(_dims(), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            0.1, FAKE, FAKE, stream=0)
+        sa.sel_attn_prefill(_dims(), FAKE + 4, *(FAKE,) * 7, 0.1, FAKE, FAKE, stream=0)
     assert e.value.code == -1
+    with pytest.raises(sa.SelAttnError) as e:   # union_rows must be 4-byte aligned
+        sa.sel_attn_prefill(_dims(), *(FAKE,) * 5, FAKE + 2, FAKE, FAKE, 0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -1 and "aligned" in sa.sel_attn_last_error()
+    with pytest.raises(sa.SelAttnError) as e:   # union_rows is required
+        sa.sel_attn_prefill(_dims(), *(FAKE,) * 5, None, FAKE, FAKE, 0.1, FAKE, FAKE, stream=0)
+    assert e.value.code == -1 and "NULL" in sa.sel_attn_last_error()
     with pytest.raises(sa.SelAttnError) as e:   # status is required
-        sa.sel_attn_prefill(_dims(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            0.1, FAKE, None, stream=0)
+        sa.sel_attn_prefill(_dims(), *(FAKE,) * 8, 0.1, FAKE, None, stream=0)
     assert e.value.code == -1
     with pytest.raises(sa.SelAttnError) as e:   # non-finite softmax scale
-        sa.sel_attn_prefill(_dims(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                            float("inf"), FAKE, FAKE, stream=0)
+        sa.sel_attn_prefill(_dims(), *(FAKE,) * 8, float("inf"), FAKE, FAKE, stream=0)
     assert e.value.code == -1
 
 
 def test_empty_query_batch_is_a_no_op():
     import sparse_top_selection_amd as sa
-    sa.sel_attn_build_union(_dims(n_q=0), None, None, None, None, None, FAKE, stream=0)
-    sa.sel_attn_prefill(_dims(n_q=0), None, None, None, None, None, None, None, None, None, 0.1,
-                        None, FAKE, stream=0)
+    sa.sel_attn_build_union(_dims(n_q=0), *(None,) * 7, FAKE, stream=0)
+    sa.sel_attn_prefill(_dims(n_q=0), *(None,) * 8, 0.1, None, FAKE, stream=0)
     sa.sel_attn_select_blocks(_dims(n_q=0, sel_cap=2051), 5, None, None, None, stream=0)
     assert sa.sel_attn_last_error() == ""
     with pytest.raises(sa.SelAttnError):   # misaligned scores
@@ -218,6 +226,7 @@ def _small_problem(n_q=10, n_kv=1, n_pages=4, cap=7):
         sel_len=torch.zeros(n_q, dtype=torch.int32),
         cells=torch.zeros(((n_q + 7) // 8, 8 * cap), dtype=torch.int32),
         mask=torch.zeros(((n_q + 7) // 8, 8 * cap), dtype=torch.uint8),
+        rows=torch.zeros(((n_q + 7) // 8, 8 * cap), dtype=torch.int32),
         length=torch.zeros((n_q + 7) // 8, dtype=torch.int32))
 
 
@@ -240,18 +249,21 @@ def test_convenience_outputs_checked_before_the_library(monkeypatch):
     p = _small_problem()
     n_ctx = 4 * 64
     pool = (p["q"], p["k_pool"], p["v_pool"], p["k_scale"], p["v_scale"], p["page_table"])
+    kv = pool[:5]   # the union call takes rows instead of the page table
     short = torch.zeros((9, 12, 128), dtype=torch.float32)
     wide_status = torch.zeros(2, dtype=torch.int32)
     u32_status = torch.zeros(1, dtype=torch.int64)
 
     cases = [
-        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx, out=short),
-        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+        lambda: sa.prefill(*kv, p["rows"], p["mask"], p["length"], 0.1, n_ctx, out=short),
+        lambda: sa.prefill(*kv, p["rows"], p["mask"], p["length"], 0.1, n_ctx,
                            out=p["q"].double()),
-        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+        lambda: sa.prefill(*kv, p["rows"], p["mask"], p["length"], 0.1, n_ctx,
                            status=wide_status),
-        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+        lambda: sa.prefill(*kv, p["rows"], p["mask"], p["length"], 0.1, n_ctx,
                            status=u32_status),
+        lambda: sa.prefill(*kv, p["rows"][:, :5], p["mask"], p["length"], 0.1, n_ctx),
+        lambda: sa.prefill(*kv, p["cells"].to(torch.int64), p["mask"], p["length"], 0.1, n_ctx),
         lambda: sa.prefill_positions(*pool, p["sel"], p["sel_len"], 0.1, n_ctx, out=short),
         lambda: sa.prefill_positions(*pool, p["sel"], p["sel_len"], 0.1, n_ctx,
                                      status=wide_status),
@@ -259,12 +271,16 @@ def test_convenience_outputs_checked_before_the_library(monkeypatch):
         lambda: sa.decode(*pool, p["sel"], p["sel_len"], 0.1, n_ctx,
                           workspace=torch.zeros(64, dtype=torch.int32)),
         lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx,
-                               out=(p["cells"][:1], p["mask"], p["length"])),
+                               out=(p["cells"][:1], p["mask"], p["rows"], p["length"])),
         lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx,
-                               out=(p["cells"], p["mask"].to(torch.int8), p["length"])),
+                               out=(p["cells"], p["mask"].to(torch.int8), p["rows"], p["length"])),
         lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx,
-                               out=(p["cells"], p["mask"], p["length"][:1])),
+                               out=(p["cells"], p["mask"], p["rows"][:1], p["length"])),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx,
+                               out=(p["cells"], p["mask"], p["rows"], p["length"][:1])),
         lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx, status=wide_status),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx, p["page_table"][:2]),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx, p["page_table"].to(torch.int64)),
         lambda: sa.select_blocks(torch.zeros((10, 4), dtype=torch.float32), 200, n_ctx,
                                  out=(p["sel"], p["sel_len"][:3])),
     ]
@@ -273,11 +289,11 @@ def test_convenience_outputs_checked_before_the_library(monkeypatch):
             case()
     # the same calls with valid arguments do reach the library
     with pytest.raises(AssertionError, match="reached the library"):
-        sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx,
+        sa.prefill(*kv, p["rows"], p["mask"], p["length"], 0.1, n_ctx,
                    out=torch.zeros_like(p["q"]), status=torch.zeros(1, dtype=torch.uint32))
     with pytest.raises(AssertionError, match="reached the library"):
-        sa.build_union(p["sel"], p["sel_len"], n_ctx,
-                       out=(p["cells"], p["mask"], p["length"]))
+        sa.build_union(p["sel"], p["sel_len"], n_ctx, p["page_table"], 1, 4,
+                       out=(p["cells"], p["mask"], p["rows"], p["length"]))
 
 
 def test_host_tensors_never_reach_the_library(monkeypatch):
@@ -297,7 +313,8 @@ def test_host_tensors_never_reach_the_library(monkeypatch):
     cases = [
         lambda: sa.select_blocks(torch.zeros((10, 4), dtype=torch.float32), 200, n_ctx),
         lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx),
-        lambda: sa.prefill(*pool, p["cells"], p["mask"], p["length"], 0.1, n_ctx),
+        lambda: sa.build_union(p["sel"], p["sel_len"], n_ctx, p["page_table"], 1, 4),
+        lambda: sa.prefill(*pool[:5], p["rows"], p["mask"], p["length"], 0.1, n_ctx),
         lambda: sa.prefill_positions(*pool, p["sel"], p["sel_len"], 0.1, n_ctx),
         lambda: sa.decode(*pool, p["sel"], p["sel_len"], 0.1, n_ctx),
         lambda: sa.attention(*pool, p["sel"], p["sel_len"], 0.1, n_ctx),
@@ -333,7 +350,7 @@ def test_prefill_split_workspace_size_and_host_errors():
     assert sa.sel_attn_prefill_workspace_bytes(capped) == 0
     assert sa.sel_attn_prefill_workspace_bytes(_dims(n_ctx=300, n_q=16, n_kv=1)) == 0
     assert sa.sel_attn_prefill_workspace_bytes(_dims(n_q=0)) == 0
-    args = (FAKE,) * 9
+    args = (FAKE,) * 8
     for ws, nbytes in ((None, 0), (FAKE, 32 * 4 * 49920 - 1)):
         with pytest.raises(sa.SelAttnError) as e:
             sa.sel_attn_prefill_split(small, *args, 0.1, FAKE, FAKE, ws, nbytes, stream=0)
@@ -341,5 +358,5 @@ def test_prefill_split_workspace_size_and_host_errors():
     with pytest.raises(sa.SelAttnError) as e:
         sa.sel_attn_prefill_split(small, *args, 0.1, FAKE, FAKE, FAKE + 8, 32 * 4 * 49920, stream=0)
     assert e.value.code == -1 and "aligned" in sa.sel_attn_last_error()
-    sa.sel_attn_prefill_split(_dims(n_q=0), *(None,) * 9, 0.1, None, FAKE, None, 0, stream=0)
+    sa.sel_attn_prefill_split(_dims(n_q=0), *(None,) * 8, 0.1, None, FAKE, None, 0, stream=0)
     assert sa.sel_attn_last_error() == ""

@@ -145,32 +145,37 @@ def test_decode_call_dominant_cell_exact(cell):
     assert_exact(out.cpu().numpy(), np.arange(pick.size), ref, "decode, cell %d" % cell)
 
 
-def test_union_path_flags_cells_out_of_range():
-    """A union cell at or past n_ctx, or negative, sets CELL_RANGE; the cell is
-    treated as not resident (dropped), every output stays finite, and the
-    groups that do not hold it are unchanged."""
-    d = synth.small_random(35, n_ctx=640, n_q=24, n_kv=1)
+def test_union_path_flags_rows_outside_the_pools():
+    """A union row whose KV-head rows would leave the pools (at or past
+    (n_pages n_kv - n_kv + 1) 64, or negative other than -1) sets PAGE_RANGE;
+    the cell is treated as not resident, every output stays finite, and the
+    groups that do not hold it are unchanged. The last row inside the limit
+    reads without a flag."""
+    d = synth.small_random(35, n_ctx=640, n_q=24, n_kv=2)
     dev = H.to_device(d)
-    cells, mask, length, status = sa.build_union(dev["sel"], dev["sel_len"], 640)
+    n_pages = d["k_pool"].shape[0]
+    cells, mask, rows, length, status = sa.build_union(dev["sel"], dev["sel_len"], 640,
+                                                       dev["page_table"], 2, n_pages)
     torch.cuda.synchronize()
     assert sa.status_value(status) == 0
     ref_out, st0 = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
-                              dev["v_scale"], dev["page_table"], cells, mask, length,
-                              float(d["softmax_scale"]), 640)
+                              dev["v_scale"], rows, mask, length, float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
     assert sa.status_value(st0) == 0
     lens = length.cpu().numpy()
-    for bad_cell in (640, 641 + 10 ** 6, -1, -5000):
-        c2 = cells.clone()
-        c2[1, int(lens[1]) // 2] = bad_cell      # group 1 only
+    limit = (n_pages * 2 - 2 + 1) * 64
+    r = ref_out.cpu().numpy()
+    keep = np.r_[0:8, 16:24]                      # groups 0 and 2
+    for bad_row, flagged in ((limit, True), (limit + 10 ** 6, True), (-2, True),
+                             (-5000, True), (limit - 1, False)):
+        print("case row", bad_row, flush=True)
+        r2 = rows.clone()
+        r2[1, int(lens[1]) // 2] = bad_row        # group 1 only
         out, st = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
-                             dev["v_scale"], dev["page_table"], c2, mask, length,
-                             float(d["softmax_scale"]), 640)
+                             dev["v_scale"], r2, mask, length, float(d["softmax_scale"]), 640)
         torch.cuda.synchronize()
         v = sa.status_value(st)
-        assert v & sa.STATUS_CELL_RANGE, (bad_cell, v)
+        assert v == (sa.STATUS_PAGE_RANGE if flagged else 0), (bad_row, v)
         o = out.cpu().numpy()
         assert np.all(np.isfinite(o))
-        r = ref_out.cpu().numpy()
-        keep = np.r_[0:8, 16:24]                  # groups 0 and 2
         assert np.array_equal(o[keep].view(np.uint32), r[keep].view(np.uint32))

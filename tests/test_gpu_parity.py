@@ -33,18 +33,44 @@ import sparse_top_selection_amd as sa  # noqa: E402
 
 
 # ----------------------------------------------------------------------------- union
+def _random_table(rng, n_ctx: int, n_pages: int, nonresident: float):
+    """A page table over n_pages physical pages: logical pages in a random
+    order, a share of them not resident (-1)."""
+    n_lp = -(-n_ctx // 64)
+    table = rng.integers(0, n_pages, size=n_lp).astype(np.int32)
+    table[rng.random(n_lp) < nonresident] = -1
+    return table
+
+
+def _union_on_gpu(sel, sel_len, n_ctx, table, n_kv, n_pages, sel_dev=None):
+    """build_union through the C ABI; numpy (cells, mask, rows, length, status)."""
+    sel_dev = torch.from_numpy(sel).cuda() if sel_dev is None else sel_dev
+    cells, mask, rows, length, status = sa.build_union(
+        sel_dev, torch.from_numpy(sel_len).cuda(), n_ctx, torch.from_numpy(table).cuda(), n_kv,
+        n_pages)
+    torch.cuda.synchronize()
+    return (cells.cpu().numpy(), mask.cpu().numpy(), rows.cpu().numpy(), length.cpu().numpy(),
+            sa.status_value(status))
+
+
+def _check_union_on_gpu(sel, sel_len, n_ctx, table, n_kv, n_pages, sel_dev=None):
+    cells, mask, rows, length, st = _union_on_gpu(sel, sel_len, n_ctx, table, n_kv, n_pages,
+                                                  sel_dev)
+    assert st == 0
+    ref = oracle.union(sel, sel_len, n_ctx)
+    H.assert_union_equal(cells, mask, length, ref)
+    ref_rows, flags = oracle.union_rows(ref[0], ref[2], table, n_kv, n_pages)
+    assert flags == 0
+    H.assert_union_rows_equal(rows, length, ref_rows)
+
+
 @pytest.mark.parametrize("idx", range(5))
 def test_union_bit_exact_on_workloads(idx):
     w = synth.workload(idx)
     d = synth.as_problem(synth.generate(w, with_q=False, with_pools=False))
     print("case", w.name, flush=True)
-    sel = torch.from_numpy(d["sel"]).cuda()
-    sel_len = torch.from_numpy(d["sel_len"]).cuda()
-    cells, mask, length, status = sa.build_union(sel, sel_len, w.n_ctx)
-    torch.cuda.synchronize()
-    assert sa.status_value(status) == 0
-    H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
-                         oracle.union(d["sel"], d["sel_len"], w.n_ctx))
+    table = _random_table(np.random.default_rng(100 + idx), w.n_ctx, w.pool_pages, 0.2)
+    _check_union_on_gpu(d["sel"], d["sel_len"], w.n_ctx, table, w.n_kv, w.pool_pages)
 
 
 @pytest.mark.parametrize("n_ctx,n_q,seed", [(300, 45, 1), (5000, 33, 2), (70000, 17, 3),
@@ -67,12 +93,9 @@ def test_union_bit_exact_edge_cases(n_ctx, n_q, seed):
             row = rng.integers(0, n_ctx, size=n).astype(np.int32)   # with repeats
         sel[j, :row.size] = row
         sel_len[j] = row.size
-    cells, mask, length, status = sa.build_union(torch.from_numpy(sel).cuda(),
-                                                 torch.from_numpy(sel_len).cuda(), n_ctx)
-    torch.cuda.synchronize()
-    assert sa.status_value(status) == 0
-    H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
-                         oracle.union(sel, sel_len, n_ctx))
+    n_pages = 1 + seed % 5
+    _check_union_on_gpu(sel, sel_len, n_ctx, _random_table(rng, n_ctx, n_pages, 0.3), 1 + seed % 3,
+                        n_pages)
 
 
 @pytest.mark.parametrize("n_ctx,n_q,cap,offset,seed", [(100, 11, 13, 1, 7), (40000, 20, 5003, 3, 8),
@@ -94,11 +117,8 @@ def test_union_bit_exact_any_row_stride_and_alignment(n_ctx, n_q, cap, offset, s
     flat[offset:offset + n_q * cap] = torch.from_numpy(sel.reshape(-1))
     dev = flat.cuda()[offset:offset + n_q * cap].view(n_q, cap)
     assert dev.data_ptr() % 16 != 0
-    cells, mask, length, status = sa.build_union(dev, torch.from_numpy(sel_len).cuda(), n_ctx)
-    torch.cuda.synchronize()
-    assert sa.status_value(status) == 0
-    H.assert_union_equal(cells.cpu().numpy(), mask.cpu().numpy(), length.cpu().numpy(),
-                         oracle.union(sel, sel_len, n_ctx))
+    _check_union_on_gpu(sel, sel_len, n_ctx, _random_table(rng, n_ctx, 50, 0.1), 4, 50,
+                        sel_dev=dev)
 
 
 def test_union_flags_bad_cells_and_lengths():
@@ -108,15 +128,34 @@ def test_union_flags_bad_cells_and_lengths():
     sel[4, 1] = 100           # outside [0, n_ctx)
     sel[6, 0] = -5
     sel_len[8] = 17           # over the cap: clamped
-    cells, mask, length, status = sa.build_union(torch.from_numpy(sel).cuda(),
-                                                 torch.from_numpy(sel_len).cuda(), 100)
-    torch.cuda.synchronize()
-    st = sa.status_value(status)
-    assert st & sa.STATUS_CELL_RANGE and st & sa.STATUS_SEL_LEN
+    table = np.array([3, 1], np.int32)
+    cells, mask, rows, length, st = _union_on_gpu(sel, sel_len, 100, table, 2, 4)
+    assert st == sa.STATUS_CELL_RANGE | sa.STATUS_SEL_LEN
     # the bad cells are dropped, the rest of the group is intact
-    assert length.cpu().tolist()[0] == 3
-    assert cells.cpu().numpy()[0, :3].tolist() == [1, 2, 3]
-    assert mask.cpu().numpy()[0, :3].tolist() == [0xFF ^ 0x40, 0xFF ^ 0x10, 0xFF]
+    assert length.tolist()[0] == 3
+    assert cells[0, :3].tolist() == [1, 2, 3]
+    assert mask[0, :3].tolist() == [0xFF ^ 0x40, 0xFF ^ 0x10, 0xFF]
+    assert rows[0, :3].tolist() == [3 * 128 + 1, 3 * 128 + 2, 3 * 128 + 3]
+
+
+@pytest.mark.parametrize("entry", [4, 1 << 30, -2, -(1 << 31)])
+def test_union_rows_flag_page_entries_outside_the_pool(entry):
+    """A page-table entry outside [-1, n_pages) sets PAGE_RANGE and gives row -1
+    for that page's cells only; -1 gives row -1 without a flag."""
+    print("case", entry, flush=True)
+    sel = np.full((12, 8), -1, np.int32)
+    sel_len = np.full(12, 4, np.int32)
+    sel[:, :4] = [5, 70, 130, 199]
+    table = np.array([3, entry, 0, -1], np.int32)
+    cells, mask, rows, length, st = _union_on_gpu(sel, sel_len, 256, table, 2, 4)
+    assert st == sa.STATUS_PAGE_RANGE
+    assert length.tolist() == [4, 4]
+    for g in range(2):
+        assert cells[g, :4].tolist() == [5, 70, 130, 199]
+        assert rows[g, :4].tolist() == [3 * 128 + 5, -1, 2, -1]
+    ref_rows, flags = oracle.union_rows(cells, length, table, 2, 4)
+    assert flags == sa.STATUS_PAGE_RANGE
+    H.assert_union_rows_equal(rows, length, ref_rows)
 
 
 # ------------------------------------------------------------------------- attention
@@ -280,25 +319,31 @@ def test_attention_bitwise_rerun_and_row_order():
 def test_attention_flags_data_errors():
     d = synth.small_random(31, n_ctx=640, n_q=16, n_kv=1)
     dev = H.to_device(d)
-    cells, mask, length, status = sa.build_union(dev["sel"], dev["sel_len"], 640)
-    torch.cuda.synchronize()
-    assert sa.status_value(status) == 0
-    # a page-table entry past the pool and a too-large v_scale
+    n_pages = d["k_pool"].shape[0]
+    # a page-table entry past the pool: flagged when the union is built, and
+    # that page's cells get row -1 (not resident)
     pt = dev["page_table"].clone()
-    pt[2] = d["n_pages"] + 5
+    pt[2] = n_pages + 5
+    cells, mask, rows, length, status = sa.build_union(dev["sel"], dev["sel_len"], 640, pt, 1,
+                                                       n_pages)
+    torch.cuda.synchronize()
+    assert sa.status_value(status) == sa.STATUS_PAGE_RANGE
+    c, r, n = cells.cpu().numpy(), rows.cpu().numpy(), length.cpu().numpy()
+    on_page_2 = [r[g, i] for g in range(n.size) for i in range(n[g]) if c[g, i] // 64 == 2]
+    assert on_page_2 and all(x == -1 for x in on_page_2)
+    # a too-large v_scale
     vs = dev["v_scale"].clone()
     vs[int(d["page_table"][0])] = 8.0
-    out, st = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], vs, pt, cells,
-                         mask, length, float(d["softmax_scale"]), 640)
+    out, st = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], vs, rows, mask,
+                         length, float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
-    v = sa.status_value(st)
-    assert v & sa.STATUS_PAGE_RANGE and v & sa.STATUS_V_SCALE
-    # a union length over the capacity is clamped and flagged
+    assert sa.status_value(st) == sa.STATUS_V_SCALE
+    # a union length over the capacity is clamped and flagged (the entries past
+    # the real union are whatever the buffer holds, so other flags may join it)
     bad_len = length.clone()
     bad_len[0] = cells.shape[1] + 1
     out, st = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
-                         dev["v_scale"], dev["page_table"], cells, mask, bad_len,
-                         float(d["softmax_scale"]), 640)
+                         dev["v_scale"], rows, mask, bad_len, float(d["softmax_scale"]), 640)
     torch.cuda.synchronize()
     assert sa.status_value(st) & sa.STATUS_UNION_LEN
 

@@ -52,10 +52,9 @@ def run_split(d: dict, dev: dict = None):
     if dev is None:
         dev = H.to_device(d)
     n_ctx = int(d["n_ctx"])
-    cells, mask, length, status = sa.build_union(dev["sel"], dev["sel_len"], n_ctx)
-    out, status = sa.prefill(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
-                             dev["v_scale"], dev["page_table"], cells, mask, length,
-                             float(d["softmax_scale"]), n_ctx, status=status, split=True)
+    out, _, status = sa.attention(dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
+                                  dev["v_scale"], dev["page_table"], dev["sel"], dev["sel_len"],
+                                  float(d["softmax_scale"]), n_ctx, split=True)
     torch.cuda.synchronize()
     n_q, n_kv = d["q"].shape[0], d["k_pool"].shape[1]
     sel_cap = d["sel"].shape[1]
