@@ -16,8 +16,11 @@
  * choose it, so every position attends to exactly its own cells.
  *
  * One pass of the path is two calls on one stream:
- *   sel_attn_build_union  selections -> per-group union, masks, lengths
- *   sel_attn_prefill      union + q + paged INT8 K/V -> attention output
+ *   sel_attn_build_union  selections + page table -> per-group union, masks,
+ *                         pool rows (each cell's page resolved once), lengths
+ *   sel_attn_prefill      union rows and masks + q + INT8 K/V pools -> output
+ * (sel_attn_prefill_split: the same attention for grids too small to fill the
+ * GPU, over a caller-owned workspace)
  * and the step before it, when the selections come from block scores:
  *   sel_attn_select_blocks  block scores -> per-position selections
  * For batches whose neighbouring selections hardly overlap, one call does the
