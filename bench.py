@@ -154,14 +154,16 @@ def counter_traffic(workload_name: str, op: str = "path"):
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
-def measured_limiter(rec, kernels, alg_bytes: float):
+def measured_limiter(rec, kernels, alg_bytes: float, sec: float):
     """What the counters say bounds the call's kernels (the first is the main
-    one): HBM traffic against their algorithmic bytes, and how busy the matrix
-    cores were."""
+    one): HBM traffic against their algorithmic bytes and against what HBM
+    could carry in the measured time, and how busy the matrix cores were."""
     if rec is None or not all(k in rec["kernels"] for k in kernels):
         return None
     traffic = sum(rec["kernels"][k]["hbm_bytes"] for k in kernels)
-    out = {"hbm_traffic_over_algorithmic_bytes": traffic / alg_bytes}
+    hbm_frac = traffic / sec / 1e9 / HBM_PEAK_GBS
+    out = {"hbm_traffic_over_algorithmic_bytes": traffic / alg_bytes,
+           "hbm_traffic_frac_of_peak": hbm_frac}
     sq = rec.get("sq", {}).get(kernels[0])
     if sq:
         d = sq["derived"]
@@ -171,8 +173,13 @@ def measured_limiter(rec, kernels, alg_bytes: float):
         out["verdict"] = ("cache-fed: HBM carries %.2fx the algorithmic bytes, so the kernel is bound by "
                           "instruction issue on the CUs (VALU, LDS and MFMA together), not by HBM"
                           % out["hbm_traffic_over_algorithmic_bytes"])
+    elif hbm_frac < 0.3:
+        out["verdict"] = ("latency-bound: HBM carries %.2fx the algorithmic bytes but at %.0f%% of its peak, "
+                          "so too few work-groups or dependent memory round trips set the time, not "
+                          "bandwidth" % (out["hbm_traffic_over_algorithmic_bytes"], 100 * hbm_frac))
     else:
-        out["verdict"] = "HBM traffic near the algorithmic bytes: bandwidth-bound"
+        out["verdict"] = ("HBM carries %.2fx the algorithmic bytes at %.0f%% of its peak: bandwidth-bound"
+                          % (out["hbm_traffic_over_algorithmic_bytes"], 100 * hbm_frac))
     return out
 
 
@@ -508,7 +515,7 @@ def main():
                 "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS},
             "mfma": {"achieved_tflops": flops / sec / 1e12, "peak_tflops": F16_MFMA_PEAK_TFLOPS,
                      "frac": flops / sec / 1e12 / F16_MFMA_PEAK_TFLOPS},
-            "measured_limiter": measured_limiter(rec, call_kernels, kv_bytes),
+            "measured_limiter": measured_limiter(rec, call_kernels, kv_bytes, sec),
         }
 
     if args.profile:

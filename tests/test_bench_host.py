@@ -65,3 +65,20 @@ def test_summaries_are_named_after_the_measured_workload():
     args = bench.parse(["--summarize", "X"])
     args.workload = bench.DEFAULT_WORKLOAD[args.op]
     assert bench.measured_workload_name(args) == "ctx32k_drift005"
+
+
+def test_measured_limiter_verdicts():
+    # cache-fed (HBM carries well under the algorithmic bytes), latency-bound
+    # (more than the algorithmic bytes, far below the HBM peak: records of a
+    # split call on a small grid) and bandwidth-bound; a call's launches add up
+    rec = {"kernels": {"k": {"hbm_bytes": 1.0e9}, "split": {"hbm_bytes": 15e6},
+                       "merge": {"hbm_bytes": 5e6}, "stream": {"hbm_bytes": 6.0e9}}}
+    v = bench.measured_limiter(rec, ("k",), 3.0e9, 0.72e-3)
+    assert v["verdict"].startswith("cache-fed")
+    v = bench.measured_limiter(rec, ("split", "merge"), 12e6, 23e-6)
+    assert abs(v["hbm_traffic_over_algorithmic_bytes"] - 20 / 12) < 1e-9
+    assert v["verdict"].startswith("latency-bound")
+    v = bench.measured_limiter(rec, ("stream",), 6.0e9, 1.0e-3)
+    assert v["verdict"].endswith("bandwidth-bound") and v["hbm_traffic_frac_of_peak"] == 0.75
+    assert bench.measured_limiter(rec, ("k", "absent"), 1.0, 1.0) is None
+    assert bench.measured_limiter(None, ("k",), 1.0, 1.0) is None
