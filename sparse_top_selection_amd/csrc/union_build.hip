@@ -57,9 +57,15 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t x) {
   return __builtin_popcount(hi & 0x80808080u);
 }
 
-// 16-byte block b of the span's aligned cover (b < n_blocks; others read block 0)
+// 16-byte block b of the span's aligned cover (b < n_blocks; others read block
+// 0). kOnce: the span is read only once (a single window), so the load is
+// marked non-temporal and does not displace cached data; with several windows
+// the span is read again from cache.
+template <bool kOnce>
 __device__ __forceinline__ i32x4 load_block(const int32_t* base, int b, int n_blocks) {
-  return *reinterpret_cast<const i32x4*>(base + 4 * (b < n_blocks ? b : 0));
+  const i32x4* p = reinterpret_cast<const i32x4*>(base + 4 * (b < n_blocks ? b : 0));
+  if constexpr (kOnce) return __builtin_nontemporal_load(p);
+  return *p;
 }
 
 // The rows of a block's four entries (f0 = flat index of entry 0 in the
@@ -132,6 +138,8 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
+// kOnce: the context fits one window (n_ctx <= kWindowCells).
+template <bool kOnce>
 __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
   __shared__ uint32_t bitmap[kWindowWords];
   __shared__ int wave_cnt[2][kWaves];
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
   // the row lengths (read next) nor the cleared bitmap until it is scattered
   i32x4 first[kBatch];
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) first[k] = load_block(base, tid + kThreads * k, n_blocks);
+  for (int k = 0; k < kBatch; ++k) first[k] = load_block<kOnce>(base, tid + kThreads * k, n_blocks);
 
   uint32_t flags = 0;
   if (tid < 8) {
@@ -214,7 +222,8 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
     for (int b0 = round == 0 ? kThreads * kBatch : 0; b0 < n_blocks; b0 += kThreads * kBatch) {
       i32x4 raw[kBatch];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k) raw[k] = load_block(base, b0 + tid + kThreads * k, n_blocks);
+      for (int k = 0; k < kBatch; ++k)
+        raw[k] = load_block<kOnce>(base, b0 + tid + kThreads * k, n_blocks);
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
         const int b = b0 + tid + kThreads * k;
@@ -296,7 +305,10 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
 
 hipError_t launch_union_build(const UnionArgs& a, hipStream_t stream) {
   const int groups = (a.n_q + 7) / 8;
-  hipLaunchKernelGGL(union_build_kernel, dim3(groups), dim3(kThreads), 0, stream, a);
+  if (a.n_ctx <= kWindowCells)
+    hipLaunchKernelGGL(union_build_kernel<true>, dim3(groups), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(union_build_kernel<false>, dim3(groups), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
