@@ -63,7 +63,7 @@ extern "C" {
 /* Return codes. */
 #define SEL_ATTN_OK 0
 #define SEL_ATTN_EINVAL (-1)       /* null or misaligned pointer, or a size out of range */
-#define SEL_ATTN_EUNSUPPORTED (-2) /* a shape this build does not implement, or a device that is not gfx950 */
+#define SEL_ATTN_EUNSUPPORTED (-2) /* a shape the library does not implement, or a device that is not gfx950 */
 #define SEL_ATTN_ELAUNCH (-3)      /* a HIP call failed (device query or kernel launch) */
 
 /* Bits the kernels OR into *status. */
@@ -74,7 +74,7 @@ extern "C" {
 #define SEL_ATTN_STATUS_UNION_LEN 8u   /* union_len[g] outside [0, 8*sel_cap] */
 #define SEL_ATTN_STATUS_V_SCALE 16u    /* a v_scale of a used cell with |v_scale| >= 4 or not finite */
 
-/* Shapes this build implements. */
+/* Shapes the library implements. */
 #define SEL_ATTN_HEAD_DIM 128
 #define SEL_ATTN_PAGE_SIZE 64
 #define SEL_ATTN_Q_PER_KV 12
