@@ -230,27 +230,46 @@ __device__ __forceinline__ void chunk_step(const PositionsArgs& a, const uint32_
   }
 }
 
+// Row i = lane & 15 of query head h*12 + i at position j (rows 12..15 read row
+// 0 and are zeroed later), dims 64q + 16g + 8hf .. +7 in x[2(2q + hf)] and the
+// next, g = lane >> 4. The kernels issue these loads before the cell list is
+// built, so that they land meanwhile.
+struct QRaw {
+  float4v x[8];
+};
+
+__device__ __forceinline__ void load_q(const PositionsArgs& a, int j, int h, int lane, QRaw& r) {
+  const int g = lane >> 4, i = lane & 15;
+  const int n_qh = a.n_kv * kQPerKv;
+  const float* qg = a.q + ((int64_t)j * n_qh + h * kQPerKv + (i < kQPerKv ? i : 0)) * kD + 16 * g;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      r.x[2 * (2 * q + hf)] = *reinterpret_cast<const float4v*>(qg + 64 * q + 8 * hf);
+      r.x[2 * (2 * q + hf) + 1] = *reinterpret_cast<const float4v*>(qg + 64 * q + 8 * hf + 4);
+    }
+}
+
 // KV head h's 12 query rows over the n cells rows[0..n): the running state,
 // with the row's probability sum and sum(P') gathered over its four lanes.
 __device__ __forceinline__ void attend_range(const PositionsArgs& a, const uint32_t* rows,
                                              WaveTile& tile, int j, int h, int n, int lane,
-                                             uint32_t& flags, ChunkState& st, float& l_row,
-                                             float& lp_row) {
-  const int g = lane >> 4, i = lane & 15;
-  const int n_qh = a.n_kv * kQPerKv;
+                                             const QRaw& qr, uint32_t& flags, ChunkState& st,
+                                             float& l_row, float& lp_row) {
+  const int i = lane & 15;
   const bool row_ok = i < kQPerKv;
 
   // Q operands of row i: k-step 2q + hf holds dims 64q + 16g + 8hf .. +7
   half8 qb[4];
   float qsum = 0.f;
   {
-    const float* qg = a.q + ((int64_t)j * n_qh + h * kQPerKv + (row_ok ? i : 0)) * kD + 16 * g;
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        float4v x0 = *reinterpret_cast<const float4v*>(qg + 64 * q + 8 * hf);
-        float4v x1 = *reinterpret_cast<const float4v*>(qg + 64 * q + 8 * hf + 4);
+        float4v x0 = qr.x[2 * (2 * q + hf)];
+        float4v x1 = qr.x[2 * (2 * q + hf) + 1];
         if (!row_ok) x0 = x1 = float4v{0.f, 0.f, 0.f, 0.f};
         const half8 v = half8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
                               (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
@@ -294,6 +313,37 @@ __device__ __forceinline__ void attend_range(const PositionsArgs& a, const uint3
   lp_row += __shfl_xor(lp_row, 32);
 }
 
+// Thread tid's entries tid + kThreads * k of position j's row (-1 past its
+// length L, which is clamped to [0, sel_cap] and flagged when outside). The
+// entries are read up to sel_cap without waiting for the length, so both reads
+// take one round trip. Returns whether this thread's entries rise strictly
+// (each below the row's next entry).
+__device__ __forceinline__ bool read_row(const PositionsArgs& a, int j, int tid, int32_t (&cell)[kPer],
+                                         int& L, uint32_t& flags) {
+  const int32_t* srow = a.sel + (int64_t)j * a.sel_cap;
+  int32_t nxt[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = tid + kThreads * k;
+    cell[k] = e < a.sel_cap ? srow[e] : -1;
+    nxt[k] = e + 1 < a.sel_cap ? srow[e + 1] : 0;
+  }
+  L = a.sel_len[j];
+  if (L < 0 || L > a.sel_cap) {
+    flags |= SEL_ATTN_STATUS_SEL_LEN;
+    L = L < 0 ? 0 : a.sel_cap;
+  }
+  bool asc = true;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = tid + kThreads * k;
+    if (e >= L) cell[k] = -1;
+    asc = asc && (e + 1 >= L || cell[k] < nxt[k]);
+    if (e < L && (cell[k] < 0 || cell[k] >= a.n_ctx)) flags |= SEL_ATTN_STATUS_CELL_RANGE;
+  }
+  return asc;
+}
+
 // Phase 1 (the whole work-group): position j's list of pool rows in sm.rows,
 // repeats, cells out of range and non-resident pages dropped, in row order.
 // Returns the list's length.
@@ -301,25 +351,10 @@ __device__ __forceinline__ int build_list(const PositionsArgs& a, Smem& sm, int 
                                           int lane, int wave, uint32_t& flags) {
   int32_t* hash_key = sm.u.hash.key;
   int32_t* hash_first = sm.u.hash.first;
-  int L = a.sel_len[j];
-  if (L < 0 || L > a.sel_cap) {
-    flags |= SEL_ATTN_STATUS_SEL_LEN;
-    L = L < 0 ? 0 : a.sel_cap;
-  }
-  const int32_t* srow = a.sel + (int64_t)j * a.sel_cap;
-
   int32_t cell[kPer];
-  bool asc = true;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int e = tid + kThreads * k;
-    cell[k] = e < L ? srow[e] : -1;
-    const int32_t next = e + 1 < L ? srow[e + 1] : 0;
-    asc = asc && (e + 1 >= L || cell[k] < next);
-    if (e < L && (cell[k] < 0 || cell[k] >= a.n_ctx)) flags |= SEL_ATTN_STATUS_CELL_RANGE;
-  }
+  int L;
   // a strictly ascending row has no repeats; any other row goes through the hash
-  const bool sorted = __syncthreads_and(asc);
+  const bool sorted = __syncthreads_and(read_row(a, j, tid, cell, L, flags));
   if (!sorted) {
     for (int s = tid; s < kHashSlots; s += kThreads) {
       hash_key[s] = -1;
@@ -399,16 +434,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(Position
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t flags = 0;
+  QRaw q0;   // Q of the first KV head this wave takes
+  if (wave < a.n_kv) load_q(a, j, wave, lane, q0);
   const int n = build_list(a, sm, j, tid, lane, wave, flags);
 
   // phase 2: wave w takes KV heads w, w + 4, ...;
   // out = (O^T - 1152 sum(P')) / (2^6 sum(p))
   const int g = lane >> 4, i = lane & 15;
   const int n_qh = a.n_kv * kQPerKv;
-  for (int h = wave; h < a.n_kv; h += kWaves) {
+  auto head = [&](int h, const QRaw& qr) {
     ChunkState st;
     float l_row, lp_row;
-    attend_range(a, sm.rows, sm.u.tile[wave], j, h, n, lane, flags, st, l_row, lp_row);
+    attend_range(a, sm.rows, sm.u.tile[wave], j, h, n, lane, qr, flags, st, l_row, lp_row);
     const float corr = 1152.f * lp_row;
     const float inv = l_row > 0.f ? (1.f / kVFold) / l_row : 0.f;
     if (i < kQPerKv) {
@@ -417,6 +454,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_positions_kernel(Position
       for (int mt = 0; mt < 8; ++mt)
         *reinterpret_cast<float4v*>(orow + 16 * mt) = (st.o[mt] - corr) * inv;
     }
+  };
+  if (wave < a.n_kv) head(wave, q0);
+  for (int h = wave + kWaves; h < a.n_kv; h += kWaves) {
+    QRaw qr;
+    load_q(a, j, h, lane, qr);
+    head(h, qr);
   }
   if (flags) atomicOr(a.status, flags);
 }
@@ -440,23 +483,9 @@ __device__ __forceinline__ int build_split_list(const PositionsArgs& a, Smem& sm
                                                 int tid, int lane, int wave, uint32_t& flags) {
   int32_t* hash_key = sm.u.hash.key;
   int32_t* hash_first = sm.u.hash.first;
-  int L = a.sel_len[j];
-  if (L < 0 || L > a.sel_cap) {
-    flags |= SEL_ATTN_STATUS_SEL_LEN;
-    L = L < 0 ? 0 : a.sel_cap;
-  }
-  const int32_t* srow = a.sel + (int64_t)j * a.sel_cap;
   int32_t cell[kPer];
-  bool asc = true;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int e = tid + kThreads * k;
-    cell[k] = e < L ? srow[e] : -1;
-    const int32_t next = e + 1 < L ? srow[e + 1] : 0;
-    asc = asc && (e + 1 >= L || cell[k] < next);
-    if (e < L && (cell[k] < 0 || cell[k] >= a.n_ctx)) flags |= SEL_ATTN_STATUS_CELL_RANGE;
-  }
-  const bool sorted = __syncthreads_and(asc);
+  int L;
+  const bool sorted = __syncthreads_and(read_row(a, j, tid, cell, L, flags));
   if (!sorted) {
     for (int s = tid; s < kHashSlots; s += kThreads) {
       hash_key[s] = -1;
@@ -519,13 +548,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(PositionsArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t flags = 0;
   const int first = kDecodeSplit * s;
+  QRaw q0;   // Q of the first KV head this wave takes
+  if (wave < a.n_kv) load_q(a, j, wave, lane, q0);
   const int n_s = build_split_list(a, sm, j, first, tid, lane, wave, flags);
 
   const int g = lane >> 4, i = lane & 15;
-  for (int h = wave; h < a.n_kv; h += kWaves) {
+  auto head = [&](int h, const QRaw& qr) {
     ChunkState st;
     float l_row, lp_row;
-    attend_range(a, sm.rows, sm.u.tile[wave], j, h, n_s, lane, flags, st, l_row, lp_row);
+    attend_range(a, sm.rows, sm.u.tile[wave], j, h, n_s, lane, qr, flags, st, l_row, lp_row);
     DecodePartial& p = part[((int64_t)j * a.n_kv + h) * a.n_splits + s];
     if (i < kQPerKv) {
       const float corr = 1152.f * lp_row;
@@ -537,6 +568,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(PositionsArgs
         p.l[i] = l_row;
       }
     }
+  };
+  if (wave < a.n_kv) head(wave, q0);
+  for (int h = wave + kWaves; h < a.n_kv; h += kWaves) {
+    QRaw qr;
+    load_q(a, j, h, lane, qr);
+    head(h, qr);
   }
   if (flags) atomicOr(a.status, flags);
 }
