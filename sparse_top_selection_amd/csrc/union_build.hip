@@ -24,9 +24,10 @@
 //     in an LDS bitmap of one byte per cell, 32K cells per window (ds_or
 //     atomics); longer contexts take several windows in ascending order, each
 //     reading the span again (from cache).
-//   * Compaction walks the window in cell order: wave w owns an eighth of it.
-//     One pass of word reads counts its nonzero bytes and marks its nonempty
-//     256-cell slabs; an eight-entry prefix over the waves gives its output
+//   * Compaction walks the window in cell order: wave w owns an eighth of its
+//     cells (rounded up to whole 256-cell slabs, so a context shorter than the
+//     window is still shared by every wave). One pass of word reads counts its
+//     nonzero bytes and marks its nonempty 256-cell slabs; an eight-entry prefix over the waves gives its output
 //     offset; then each nonempty slab is emitted 64 cells at a time (byte
 //     reads, ballot, mbcnt), so that consecutive lanes store consecutive union
 //     entries. The 64 cells of one emission step lie in one logical page, so
@@ -233,24 +234,27 @@ __global__ __launch_bounds__(kThreads, 8) void union_build_kernel(UnionArgs a) {
                         w0, win);
       }
     }
-    // this wave's share of the window covers logical pages pw .. pw + 63 (its
-    // 16 slabs of 256 cells): lane l reads entry pw + l now, and emission takes
-    // entry 4s + k of slab s, step k from that lane (clamped to the table; a
-    // page past the context holds no union cell)
-    const int pw = (w0 + 4 * wave * kWaveWords) >> 6;
+    // this wave's share of the window: words [wb, wb + share), an eighth of
+    // the window's words rounded up to whole slabs of 64 words (256 cells), at
+    // most 16 slabs, so that short contexts keep every wave busy. It covers
+    // logical pages pw .. pw + 63 at most: lane l reads entry pw + l now, and
+    // emission takes entry 4s + k of slab s, step k from that lane (clamped to
+    // the table; a page past the context holds no union cell)
+    const int words = (win + 3) >> 2;
+    const int share = min(kWaveWords, ((words + kWaves - 1) / kWaves + 63) & ~63);
+    const int wb = wave * share;
+    const int pw = (w0 + 4 * wb) >> 6;
     const int32_t page_of_lane = a.page_table[min(pw + lane, last_page)];
     __syncthreads();
 
-    // compaction of this wave's share of the window: words
-    // [wave * kWaveWords, +kWaveWords), slabs of 64 words (256 cells). One
-    // pass of word reads counts the nonzero bytes and marks the nonempty slabs.
-    const int words = (win + 3) >> 2;
-    const int wb = wave * kWaveWords;
+    // compaction of this wave's share. One pass of word reads counts the
+    // nonzero bytes and marks the nonempty slabs.
+    const int lim = min(share, words - wb);   // words of the share inside the window
     int cnt = 0;
     uint32_t nonempty = 0;   // bit s: slab s holds a union cell (same in every lane)
 #pragma unroll
     for (int s = 0; s < kSlabs; ++s) {
-      const uint32_t x = (wb + 64 * s < words) ? bitmap[wb + 64 * s + lane] : 0u;
+      const uint32_t x = (64 * s < lim) ? bitmap[wb + 64 * s + lane] : 0u;
       cnt += nonzero_bytes(x);
       nonempty |= __ballot(x != 0u) ? (1u << s) : 0u;
     }
