@@ -55,6 +55,30 @@ DEFAULT_WORKLOAD = {"path": "ctx32k_drift005", "select": "ctx32k_drift005",
 # selection entry and page-table entry; q and out as for the path
 POS_CELL_BYTES = 128 + 128 + 4 + 4
 POS_ENTRY_BYTES = 4 + 4
+# Untimed back-to-back steps before the warm-up steps. The GPU idles while the
+# host builds the inputs, and its shader clock then needs tens of milliseconds of
+# load to climb back: after a 5-step warm-up the 32K prefill timed 0.736-0.740 ms,
+# after 50 or 200 steps 0.703-0.705 ms (one machine, same build).
+SETTLE_MS = 100.0
+SETTLE_WHY = ("untimed back-to-back steps until the GPU has run them for %.0f ms, before the warm-up "
+              "steps: the shader clock climbs back from the idle of the input set-up" % SETTLE_MS)
+
+
+def settle(step, min_ms: float = SETTLE_MS, max_steps: int = 20000) -> dict:
+    """Run `step` untimed, ten at a time, until min_ms of wall time have passed
+    (or max_steps); returns what was run, for the JSON line."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_steps:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            break
+    return {"steps": n, "ms": round((time.perf_counter() - t0) * 1e3, 1), "why": SETTLE_WHY}
 
 
 def parse(argv=None):
@@ -437,6 +461,7 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    settled = None if args.profile else settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -535,7 +560,7 @@ def main():
         "unit": "query-head-cells/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "settle": settled,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -636,6 +661,7 @@ def bench_decode(args):
                            t["page_table"], t["sel"], t["sel_len"], scale, out, ws, ws_bytes,
                            status, stream)
 
+    settled = None if args.profile else settle(launch)
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
@@ -672,7 +698,7 @@ def bench_decode(args):
     result = {
         "metric": "decode attention latency (%d position%s at the end of %s)" % (
             nd, "" if nd == 1 else "s", w.name),
-        "value": us, "unit": "us", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "value": us, "unit": "us", "n_gpus": 1, "steps": steps, "warmup": args.warmup, "settle": settled,
         "ms_per_step": us * 1e-3, "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8 K/V, fp16 products, fp32 softmax and sums",
         "data": "synthetic (seeded; the workload's last positions)",
@@ -730,6 +756,7 @@ def bench_select(args):
     def launch():
         sa.sel_attn_select_blocks(dims, first, scores, sel, sel_len, stream)
 
+    settled = None if args.profile else settle(launch)
     for _ in range(args.warmup):
         launch()
     torch.cuda.synchronize()
@@ -768,7 +795,7 @@ def bench_select(args):
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "settle": settled,
         "ms_per_step": kern_ms,
         "higher_is_better": True,
         "scaling": "weak",
